@@ -1,0 +1,208 @@
+"""Benchmark: Engram prefill forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step = one engram_forward (hash -> fp8 row gather -> wkv bf16 MFMA
+projection -> gate and add) over the DeepSeek-V4.1-shaped prefill: B=1,
+T=4096, dim=5120, hc=4, 24 hash columns of head_dim 64 (wkv 1536 -> 25600),
+a 25,160,950-row fp8 table, seeded synthetic inputs already resident in HBM.
+Prints one JSON line: whole-job tokens/s, the wkv kernel's roofline
+(flops per launch over its average launch time, measured here with HIP events
+on the stream it runs on) and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Engram prefill tokens/s @dim5120 hc4 (1 GPU); % MFMA peak (wkv), % HBM BW (gate)"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "wkv_prefill_traffic.json")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample", type=int, default=2048, help="tokens the oracle runs")
+    return p.parse_args()
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gram_memory_layer_amd", "csrc")
+    for f in ("wkv.hip", "internal.h"):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(launch_flops_tokens: int):
+    """HBM bytes per wkv launch from the committed rocprofv3 counter summary,
+    or None if it was taken on a different kernel source or workload."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_digest") != kernel_source_digest() or rec.get("tokens") != launch_flops_tokens:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def time_launches(fn, n, stream):
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(n):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / n * 1e-3  # seconds per launch
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: every box in this setup has one, and the "
+              "Engram path is measured per GPU (see DESIGN.md for how it would shard).",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import gram_memory_layer_amd as ge
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = synth.config("prefill")
+    t = synth.hash_tables(cfg)
+    g = ge.Geometry.make(cfg.dim, cfg.hc_mult, cfg.max_ngram_size, cfg.n_heads, cfg.head_dim,
+                         t["num_embeddings"], cfg.vocab, cfg.pad_id, cfg.norm_eps)
+    tables = {k: torch.from_numpy(t[k]).to(dev) for k in ("token_map", "mult", "prime", "offset")}
+    table, scales = synth.embedding_table(cfg, t["num_embeddings"], dev)
+    w = synth.wkv_weight(cfg, dev)
+    q, k = synth.qk_weights(cfg, dev)
+    B, T = cfg.B, cfg.T
+    n_tok = B * T
+    ids_np = synth.token_ids(cfg, B, T)
+    ids = torch.from_numpy(ids_np).to(dev)
+    x = synth.activations(cfg, n_tok, dev).reshape(B, T, cfg.hc_mult, cfg.dim)
+    mask = torch.from_numpy(synth.token_mask(cfg, B, T)).to(dev)
+    out = torch.empty_like(x)
+    layer = ge.EngramLayer(g, tables, table, scales, w, q, k)
+    ws = layer.workspace(n_tok)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        ge.engram_forward(g, tables, table, scales, w, q, k, x, ids, mask=mask, out=out,
+                          workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    sec = time_launches(step, args.steps, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tokens_per_s = n_tok / sec
+
+    # ---- per-stage launch times (each stage alone, same inputs, same stream)
+    hid = ge.engram_hash(g, tables, ids)
+    rows = ge.engram_gather(g, table, scales, hid)
+    kv = ge.engram_wkv(g, rows, w)
+    ge.engram_gate_add(g, x, kv, q, k, mask=mask, out=out)
+    torch.cuda.synchronize()
+    reps = max(args.steps, 10)
+    st_hash = time_launches(lambda: ge.engram_hash(g, tables, ids, hash_ids=hid), reps, stream)
+    st_gather = time_launches(lambda: ge.engram_gather(g, table, scales, hid, rows=rows), reps, stream)
+    st_wkv = time_launches(lambda: ge.engram_wkv(g, rows, w, kv=kv), reps, stream)
+    st_gate = time_launches(lambda: ge.engram_gate_add(g, x, kv, q, k, mask=mask, out=out), reps,
+                            stream)
+
+    flops_per_token = 2 * g.K * g.N
+    wkv_flops = flops_per_token * n_tok
+    achieved = wkv_flops / st_wkv / 1e12
+    traffic = traffic_record(n_tok)
+    gate_bytes = n_tok * (2 * g.hc_mult * g.dim * 2 + g.N * 2)
+    rec = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Engram prefill forward, B=1 T=4096, dim=5120 hc=4, 24 hash cols x "
+                               "head_dim 64 (wkv 1536->25600), 25,160,950-row fp8 e4m3 table",
+                   "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
+        "roofline": {"kernel": "wkv", "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+        "stages_us": {"hash": round(st_hash * 1e6, 2), "gather": round(st_gather * 1e6, 2),
+                      "wkv": round(st_wkv * 1e6, 2), "gate_add": round(st_gate * 1e6, 2)},
+        "gate_hbm": {"achieved": round(gate_bytes / st_gate / 1e9, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gate_bytes / st_gate / 1e9 / PEAK_HBM_GBS, 4)},
+        "wall_s": round(wall, 3),
+    }
+
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(cfg, t, table, scales, w, q, k, x, ids_np, mask,
+                                           args.cpu_sample)
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(cfg, t, table, scales, w, q, k, x, ids_np, mask, n_sample):
+    """The oracle on the first `n_sample` positions of the same workload:
+    hash (whole prefix it needs), row gather, fp64 projection, gate."""
+    import numpy as np
+    import torch
+
+    import oracle
+    b = lambda z: z.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    S = n_sample
+    hid = None
+    geom = {"max_ngram_size": cfg.max_ngram_size, "n_heads": cfg.n_heads, "vocab": cfg.vocab,
+            "pad_id": cfg.pad_id, "hc_mult": cfg.hc_mult, "dim": cfg.dim,
+            "norm_eps": cfg.norm_eps}
+    # the rows the sample touches, copied out of the device table (input bytes)
+    st = oracle.HashState(1, S + 8)
+    hid = oracle.hash_ids(t, geom, st, ids_np[:, :S])
+    uniq, inv = np.unique(hid.reshape(-1), return_inverse=True)
+    idx = torch.from_numpy(uniq.astype(np.int64)).to(table.device)
+    tab = table.index_select(0, idx).cpu().numpy()
+    sc = scales.index_select(0, idx).cpu().numpy()
+    wb, qb, kb = b(w), b(q), b(k)
+    xb = b(x.reshape(-1, cfg.hc_mult, cfg.dim)[:S])
+    mk = mask.reshape(-1)[:S].cpu().numpy()
+    t0 = time.perf_counter()
+    st = oracle.HashState(1, S + 8)
+    h = oracle.hash_ids(t, geom, st, ids_np[:, :S])
+    _, inv = np.unique(h.reshape(-1), return_inverse=True)
+    rows = oracle.embed_rows(tab, sc, inv.astype(np.int32)).reshape(S, -1)
+    kv = oracle.linear(rows, wb)
+    oracle.gate_and_add(xb, kv, qb, kb, cfg.norm_eps, mk)
+    el = time.perf_counter() - t0
+    return {"value": round(S / el, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "sample": "first %d positions of the T=4096 prefill (all four "
+                                        "stages, fp64), %.1f s" % (S, el)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,171 @@
+// The C ABI of libengram: argument validation, launch dispatch and the fused
+// forward.  All checks happen on the host before anything is enqueued.
+#include <math.h>
+#include <string.h>
+
+#include "internal.h"
+
+namespace engram {
+
+Geom make_geom(const engram_geometry& g) {
+    Geom o;
+    o.dim = g.dim;
+    o.hc = g.hc_mult;
+    o.max_ngram = g.max_ngram_size;
+    o.n_heads = g.n_heads;
+    o.head_dim = g.head_dim;
+    o.n_cols = (g.max_ngram_size - 1) * g.n_heads;
+    o.K = o.n_cols * g.head_dim;
+    o.N = g.dim * (g.hc_mult + 1);
+    o.vocab = g.vocab;
+    o.pad_id = g.pad_id;
+    o.num_embeddings = g.num_embeddings;
+    o.eps = g.norm_eps;
+    return o;
+}
+
+}  // namespace engram
+
+using engram::Geom;
+
+namespace {
+
+constexpr int64_t kMaxTokens = (int64_t)1 << 31;
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+engram_status from_hip(hipError_t e) { return e == hipSuccess ? ENGRAM_OK : ENGRAM_ERR_HIP; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* engram_status_string(engram_status s) {
+    switch (s) {
+        case ENGRAM_OK: return "ok";
+        case ENGRAM_ERR_INVALID_ARG: return "invalid argument";
+        case ENGRAM_ERR_UNSUPPORTED: return "unsupported geometry";
+        case ENGRAM_ERR_WORKSPACE: return "workspace missing or too small";
+        case ENGRAM_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+engram_status engram_check_geometry(const engram_geometry* g) {
+    if (g == nullptr) return ENGRAM_ERR_INVALID_ARG;
+    if (g->reserved != 0 || g->reserved2 != 0) return ENGRAM_ERR_INVALID_ARG;
+    if (g->dim < 8 || g->dim > 65536 || g->dim % 8 != 0) return ENGRAM_ERR_UNSUPPORTED;
+    if (g->hc_mult < 1 || g->hc_mult > 8) return ENGRAM_ERR_UNSUPPORTED;
+    if (g->max_ngram_size < 2 || g->max_ngram_size > 16) return ENGRAM_ERR_UNSUPPORTED;
+    if (g->n_heads < 1 || (int64_t)(g->max_ngram_size - 1) * g->n_heads > 1024)
+        return ENGRAM_ERR_UNSUPPORTED;
+    if (g->head_dim < 32 || g->head_dim > 1024 || g->head_dim % 32 != 0)
+        return ENGRAM_ERR_UNSUPPORTED;
+    if (g->num_embeddings < 1 || g->num_embeddings > INT32_MAX) return ENGRAM_ERR_UNSUPPORTED;
+    if (g->vocab < 1) return ENGRAM_ERR_INVALID_ARG;
+    if (!(g->norm_eps >= 0.0f) || !isfinite(g->norm_eps)) return ENGRAM_ERR_INVALID_ARG;
+    return ENGRAM_OK;
+}
+
+engram_status engram_hash(const engram_geometry* g, const engram_hash_tables* t, int32_t* state,
+                          const int32_t* ids, int32_t B, int32_t T, int32_t* hash_ids,
+                          uint32_t* err, void* stream) {
+    engram_status st = engram_check_geometry(g);
+    if (st != ENGRAM_OK) return st;
+    if (t == nullptr || B < 0 || T < 0) return ENGRAM_ERR_INVALID_ARG;
+    if ((int64_t)B * T >= kMaxTokens) return ENGRAM_ERR_INVALID_ARG;
+    if ((int64_t)B * T == 0) return ENGRAM_OK;
+    if (!t->token_map || !t->mult || !t->prime || !t->offset || !ids || !hash_ids)
+        return ENGRAM_ERR_INVALID_ARG;
+    const Geom gg = engram::make_geom(*g);
+    return from_hip(engram::launch_hash(gg, *t, state, ids, B, T, hash_ids, err,
+                                        (hipStream_t)stream));
+}
+
+engram_status engram_gather(const engram_geometry* g, const uint8_t* table, const uint8_t* scales,
+                            const int32_t* hash_ids, int64_t n_tok, uint16_t* rows,
+                            uint32_t* err, void* stream) {
+    engram_status st = engram_check_geometry(g);
+    if (st != ENGRAM_OK) return st;
+    if (n_tok < 0 || n_tok >= kMaxTokens) return ENGRAM_ERR_INVALID_ARG;
+    if (n_tok == 0) return ENGRAM_OK;
+    if (!table || !scales || !hash_ids || !rows) return ENGRAM_ERR_INVALID_ARG;
+    if (((uintptr_t)table & 7u) != 0 || !aligned16(rows)) return ENGRAM_ERR_INVALID_ARG;
+    const Geom gg = engram::make_geom(*g);
+    return from_hip(engram::launch_gather(gg, table, scales, hash_ids, n_tok, rows, err,
+                                          (hipStream_t)stream));
+}
+
+engram_status engram_wkv(const engram_geometry* g, const uint16_t* a, const uint16_t* w,
+                         int64_t M, uint16_t* kv, void* stream) {
+    engram_status st = engram_check_geometry(g);
+    if (st != ENGRAM_OK) return st;
+    if (M < 0 || M >= kMaxTokens) return ENGRAM_ERR_INVALID_ARG;
+    if (M == 0) return ENGRAM_OK;
+    if (!a || !w || !kv) return ENGRAM_ERR_INVALID_ARG;
+    if (!aligned16(a) || !aligned16(w) || ((uintptr_t)kv & 7u) != 0) return ENGRAM_ERR_INVALID_ARG;
+    const Geom gg = engram::make_geom(*g);
+    return from_hip(engram::launch_wkv(a, w, M, gg.N, gg.K, kv, (hipStream_t)stream));
+}
+
+engram_status engram_gate_add(const engram_geometry* g, const uint16_t* x, const uint16_t* kv,
+                              const uint16_t* q, const uint16_t* k, const uint8_t* mask,
+                              int64_t n_tok, uint16_t* out, float* gate, void* stream) {
+    engram_status st = engram_check_geometry(g);
+    if (st != ENGRAM_OK) return st;
+    if (n_tok < 0 || n_tok >= kMaxTokens) return ENGRAM_ERR_INVALID_ARG;
+    if (n_tok == 0) return ENGRAM_OK;
+    if (!x || !kv || !q || !k || !out) return ENGRAM_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(kv) || !aligned16(q) || !aligned16(k) || !aligned16(out))
+        return ENGRAM_ERR_INVALID_ARG;
+    const Geom gg = engram::make_geom(*g);
+    return from_hip(engram::launch_gate_add(gg, x, kv, q, k, mask, n_tok, out, gate,
+                                            (hipStream_t)stream));
+}
+
+size_t engram_forward_workspace_size(const engram_geometry* g, int64_t n_tok) {
+    if (engram_check_geometry(g) != ENGRAM_OK || n_tok < 0) return 0;
+    const Geom gg = engram::make_geom(*g);
+    return align256((size_t)n_tok * gg.n_cols * sizeof(int32_t)) +
+           align256((size_t)n_tok * gg.K * sizeof(uint16_t)) +
+           align256((size_t)n_tok * gg.N * sizeof(uint16_t));
+}
+
+engram_status engram_forward(const engram_geometry* g, const engram_hash_tables* t,
+                             const uint8_t* table, const uint8_t* scales, const uint16_t* w,
+                             const uint16_t* q, const uint16_t* k, int32_t* state,
+                             const uint16_t* x, const int32_t* ids, const uint8_t* mask,
+                             int32_t B, int32_t T, uint16_t* out, float* gate, void* workspace,
+                             size_t workspace_bytes, uint32_t* err, void* stream) {
+    engram_status st = engram_check_geometry(g);
+    if (st != ENGRAM_OK) return st;
+    if (t == nullptr || B < 0 || T < 0) return ENGRAM_ERR_INVALID_ARG;
+    const int64_t n_tok = (int64_t)B * T;
+    if (n_tok >= kMaxTokens) return ENGRAM_ERR_INVALID_ARG;
+    if (n_tok == 0) return ENGRAM_OK;
+    if (!t->token_map || !t->mult || !t->prime || !t->offset || !ids) return ENGRAM_ERR_INVALID_ARG;
+    if (!table || !scales || !w || !q || !k || !x || !out) return ENGRAM_ERR_INVALID_ARG;
+    if (((uintptr_t)table & 7u) != 0 || !aligned16(w) || !aligned16(q) || !aligned16(k) ||
+        !aligned16(x) || !aligned16(out))
+        return ENGRAM_ERR_INVALID_ARG;
+    const size_t need = engram_forward_workspace_size(g, n_tok);
+    if (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
+        return ENGRAM_ERR_WORKSPACE;
+    const Geom gg = engram::make_geom(*g);
+    char* ws = (char*)workspace;
+    int32_t* hash_ids = (int32_t*)ws;
+    ws += align256((size_t)n_tok * gg.n_cols * sizeof(int32_t));
+    uint16_t* rows = (uint16_t*)ws;
+    ws += align256((size_t)n_tok * gg.K * sizeof(uint16_t));
+    uint16_t* kv = (uint16_t*)ws;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = engram::launch_hash(gg, *t, state, ids, B, T, hash_ids, err, s);
+    if (e == hipSuccess) e = engram::launch_gather(gg, table, scales, hash_ids, n_tok, rows, err, s);
+    if (e == hipSuccess) e = engram::launch_wkv(rows, w, n_tok, gg.N, gg.K, kv, s);
+    if (e == hipSuccess) e = engram::launch_gate_add(gg, x, kv, q, k, mask, n_tok, out, gate, s);
+    return from_hip(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,209 @@
+// Stage 4: gate and add ("Module engram" docs, gate_and_add; the Engram
+// block's forward after the projection; "Gate per stream" equations for a_k
+// and g).
+//
+// One workgroup per token.  Each thread owns NCH 16-byte chunks (8 features)
+// of every stream and of the shared value: it loads them once, keeps x and
+// the value in registers, accumulates its share of the 3*HC sums
+//   S_hh[s] = sum h^2,  S_kk[s] = sum key^2,  S_hwk[s] = sum (h*w)*key,
+// and after a fixed-order block reduction writes out = bf16(h + g[s]*v) from
+// the registers it already holds.  HBM traffic is the algorithmic minimum:
+// x and kv read once, out written once (q and k are L2-resident).
+//
+// x and out may be the same buffer: every thread writes only the chunks it
+// has itself read, after reading them (so neither pointer is __restrict__).
+//
+// Numerics: fp32.  h*w is exact in fp32 (8 + 16 significand bits); the
+// product with key is rounded and then added (no fused multiply-add), as an
+// elementwise product followed by a sum does, so an exactly cancelling pair
+// of terms sums to exactly +0.  Reductions are in a fixed tree order, so the
+// result is the same on every run.
+#include "internal.h"
+
+namespace engram {
+namespace {
+
+__device__ __forceinline__ float lo_f(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float hi_f(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+template <int HC, int NCH>
+__global__ void __launch_bounds__(1024) gate_kernel(
+    const uint16_t* x, const uint16_t* __restrict__ kv,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kw,
+    const uint8_t* __restrict__ mask, int dim, float eps, float inv_sqrt_dim,
+    uint16_t* out, float* __restrict__ gate) {
+#pragma clang fp contract(off)
+    constexpr int NS = 3 * HC;
+    __shared__ float red[16][NS];
+    __shared__ float gsh[HC];
+
+    const int64_t tok = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int nthr = blockDim.x;
+    const int d8 = dim / 8;
+    const int64_t row = (int64_t)dim * (HC + 1);
+    const uint16_t* xt = x + tok * HC * dim;
+    const uint16_t* kvt = kv + tok * row;
+    uint16_t* ot = out + tok * HC * dim;
+    const bool live = (mask == nullptr) || (mask[tok] != 0);
+
+    uint4 xr[HC][NCH];
+    if (!live) {
+        // masked position: the gate is 0 and x passes through unchanged
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            const int c = tid + i * nthr;
+            if (c < d8)
+#pragma unroll
+                for (int s = 0; s < HC; ++s) {
+                    const uint4 u = *reinterpret_cast<const uint4*>(xt + (int64_t)s * dim + c * 8);
+                    *reinterpret_cast<uint4*>(ot + (int64_t)s * dim + c * 8) = u;
+                }
+        }
+        if (gate && tid < HC) gate[tok * HC + tid] = 0.0f;
+        return;
+    }
+
+    float acc[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) acc[j] = 0.0f;
+    uint4 vr[NCH];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const int c = tid + i * nthr;
+        if (c < d8) {
+            vr[i] = *reinterpret_cast<const uint4*>(kvt + (int64_t)HC * dim + c * 8);
+#pragma unroll
+            for (int s = 0; s < HC; ++s) {
+                const uint4 h = *reinterpret_cast<const uint4*>(xt + (int64_t)s * dim + c * 8);
+                const uint4 key = *reinterpret_cast<const uint4*>(kvt + (int64_t)s * dim + c * 8);
+                const uint4 qq = *reinterpret_cast<const uint4*>(q + (int64_t)s * dim + c * 8);
+                const uint4 kk = *reinterpret_cast<const uint4*>(kw + (int64_t)s * dim + c * 8);
+                xr[s][i] = h;
+                const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
+                const uint32_t kyw[4] = {key.x, key.y, key.z, key.w};
+                const uint32_t qw[4] = {qq.x, qq.y, qq.z, qq.w};
+                const uint32_t kw4[4] = {kk.x, kk.y, kk.z, kk.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float h0 = lo_f(hw[e]), h1 = hi_f(hw[e]);
+                    const float k0 = lo_f(kyw[e]), k1 = hi_f(kyw[e]);
+                    const float w0 = lo_f(qw[e]) * lo_f(kw4[e]);
+                    const float w1 = hi_f(qw[e]) * hi_f(kw4[e]);
+                    acc[s] += h0 * h0;
+                    acc[s] += h1 * h1;
+                    acc[HC + s] += k0 * k0;
+                    acc[HC + s] += k1 * k1;
+                    const float p0 = (h0 * w0) * k0;
+                    const float p1 = (h1 * w1) * k1;
+                    acc[2 * HC + s] += p0;
+                    acc[2 * HC + s] += p1;
+                }
+            }
+        }
+    }
+
+    // fixed-order block reduction
+    const int lane = tid & 63, wave = tid >> 6, nwaves = (nthr + 63) >> 6;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        const float v = wave_sum(acc[j]);
+        if (lane == 0) red[wave][j] = v;
+    }
+    __syncthreads();
+    if (tid < HC) {
+        float shh = 0.f, skk = 0.f, shwk = 0.f;
+        for (int w = 0; w < nwaves; ++w) {
+            shh += red[w][tid];
+            skk += red[w][HC + tid];
+            shwk += red[w][2 * HC + tid];
+        }
+        const float fd = (float)dim;
+        const float rstd = (1.0f / sqrtf(shh / fd + eps)) * (1.0f / sqrtf(skk / fd + eps));
+        const float a = shwk * rstd * inv_sqrt_dim;
+        const float mag = fmaxf(fabsf(a), 1e-6f);
+        const float sg = copysignf(sqrtf(mag), a);
+        const float g = 1.0f / (1.0f + expf(-sg));
+        gsh[tid] = g;
+        if (gate) gate[tok * HC + tid] = g;
+    }
+    __syncthreads();
+
+    float g[HC];
+#pragma unroll
+    for (int s = 0; s < HC; ++s) g[s] = gsh[s];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const int c = tid + i * nthr;
+        if (c < d8) {
+            const uint32_t vw[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+#pragma unroll
+            for (int s = 0; s < HC; ++s) {
+                const uint32_t hw[4] = {xr[s][i].x, xr[s][i].y, xr[s][i].z, xr[s][i].w};
+                uint32_t o[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float r0 = __fmaf_rn(g[s], lo_f(vw[e]), lo_f(hw[e]));
+                    const float r1 = __fmaf_rn(g[s], hi_f(vw[e]), hi_f(hw[e]));
+                    o[e] = f32_to_bf16(r0) | (f32_to_bf16(r1) << 16);
+                }
+                *reinterpret_cast<uint4*>(ot + (int64_t)s * dim + c * 8) =
+                    make_uint4(o[0], o[1], o[2], o[3]);
+            }
+        }
+    }
+}
+
+template <int HC>
+hipError_t run_hc(const Geom& g, const uint16_t* x, const uint16_t* kv, const uint16_t* q,
+                  const uint16_t* k, const uint8_t* mask, int64_t n_tok, uint16_t* out,
+                  float* gate, hipStream_t s) {
+    const int d8 = g.dim / 8;
+    int nch = 1;
+    while (nch < 8 && (d8 + nch - 1) / nch > 512) nch *= 2;
+    int threads = (d8 + nch - 1) / nch;
+    threads = (threads + 63) / 64 * 64;
+    const float inv_sqrt_dim = (float)(1.0 / sqrt((double)g.dim));
+    const dim3 grid((unsigned)n_tok), block(threads);
+#define ENGRAM_GATE_CASE(N)                                                                  \
+    case N:                                                                                  \
+        gate_kernel<HC, N><<<grid, block, 0, s>>>(x, kv, q, k, mask, g.dim, g.eps,           \
+                                                  inv_sqrt_dim, out, gate);                  \
+        break;
+    switch (nch) {
+        ENGRAM_GATE_CASE(1)
+        ENGRAM_GATE_CASE(2)
+        ENGRAM_GATE_CASE(4)
+        ENGRAM_GATE_CASE(8)
+        default: return hipErrorInvalidValue;
+    }
+#undef ENGRAM_GATE_CASE
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gate_add(const Geom& g, const uint16_t* x, const uint16_t* kv,
+                           const uint16_t* q, const uint16_t* k, const uint8_t* mask,
+                           int64_t n_tok, uint16_t* out, float* gate, hipStream_t s) {
+    if (n_tok == 0) return hipSuccess;
+    switch (g.hc) {
+        case 1: return run_hc<1>(g, x, kv, q, k, mask, n_tok, out, gate, s);
+        case 2: return run_hc<2>(g, x, kv, q, k, mask, n_tok, out, gate, s);
+        case 3: return run_hc<3>(g, x, kv, q, k, mask, n_tok, out, gate, s);
+        case 4: return run_hc<4>(g, x, kv, q, k, mask, n_tok, out, gate, s);
+        case 5: return run_hc<5>(g, x, kv, q, k, mask, n_tok, out, gate, s);
+        case 6: return run_hc<6>(g, x, kv, q, k, mask, n_tok, out, gate, s);
+        case 7: return run_hc<7>(g, x, kv, q, k, mask, n_tok, out, gate, s);
+        case 8: return run_hc<8>(g, x, kv, q, k, mask, n_tok, out, gate, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace engram

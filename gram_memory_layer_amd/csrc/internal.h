@@ -1,0 +1,51 @@
+// Internal interfaces between the C ABI (api.hip) and the kernels.
+// gfx950 only: wave64, bf16 MFMA, 160 KiB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "engram.h"
+
+namespace engram {
+
+// bf16 <-> fp32 bit helpers (bf16 is the top half of an IEEE binary32).
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) {
+    return __uint_as_float(b << 16);
+}
+
+// fp32 -> bf16, round to nearest even; NaN -> canonical 0x7FC0.  The add of
+// 0x7FFF plus the kept LSB rounds ties to even, carries into the exponent
+// when the mantissa overflows and reaches infinity past the largest finite
+// value; subnormals round on the same integer grid.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+struct Geom {
+    int dim, hc, max_ngram, n_heads, head_dim, n_cols, K, N;
+    int vocab, pad_id;
+    int64_t num_embeddings;
+    float eps;
+};
+
+Geom make_geom(const engram_geometry& g);
+
+hipError_t launch_hash(const Geom& g, const engram_hash_tables& t, int32_t* state,
+                       const int32_t* ids, int B, int T, int32_t* hash_ids, uint32_t* err,
+                       hipStream_t s);
+
+hipError_t launch_gather(const Geom& g, const uint8_t* table, const uint8_t* scales,
+                         const int32_t* hash_ids, int64_t n_tok, uint16_t* rows, uint32_t* err,
+                         hipStream_t s);
+
+hipError_t launch_wkv(const uint16_t* a, const uint16_t* w, int64_t M, int N, int K,
+                      uint16_t* kv, hipStream_t s);
+
+hipError_t launch_gate_add(const Geom& g, const uint16_t* x, const uint16_t* kv,
+                           const uint16_t* q, const uint16_t* k, const uint8_t* mask,
+                           int64_t n_tok, uint16_t* out, float* gate, hipStream_t s);
+
+}  // namespace engram

@@ -1,0 +1,161 @@
+/*
+ * libengram -- the Engram forward path on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Every tensor argument is a DEVICE pointer owned by the caller; the
+ * library allocates nothing, keeps no pointer after a call returns and never
+ * synchronises.  Every call validates its arguments on the host first: on an
+ * error it returns a status and launches nothing.  Work is enqueued on
+ * `stream` (a hipStream_t; NULL means the legacy default stream) and runs
+ * asynchronously; a HIP launch failure is reported as ENGRAM_ERR_HIP.
+ *
+ * Data-dependent errors (a token id outside [0, vocab), a hash id outside
+ * [0, num_embeddings)) cannot be seen on the host.  The kernels OR the
+ * ENGRAM_ERRBIT_* flags into the optional device word `err` (uint32, caller
+ * zeroes it; NULL = do not report) and still write well-defined output: a bad
+ * token is treated as the pad id, and a bad row id gathers a row of zeros.
+ * No kernel ever reads outside its inputs.
+ *
+ * Layouts are row-major and dense.  bf16 tensors are passed as uint16_t bit
+ * patterns.  Names follow the pages that describe the method:
+ *   [block] the DeepSeek V4.1 Engram block listing (constructor and forward);
+ *   [gate]  the "Gate per stream" page (equations for a_k and g, in/out box);
+ *   [docs]  the "Module engram" CPU-reference docs (four stages, structs,
+ *           functions).
+ */
+#ifndef ENGRAM_H
+#define ENGRAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum engram_status {
+    ENGRAM_OK = 0,
+    ENGRAM_ERR_INVALID_ARG = 1,   /* null pointer, negative size, bad shape */
+    ENGRAM_ERR_UNSUPPORTED = 2,   /* geometry outside what the kernels handle */
+    ENGRAM_ERR_WORKSPACE = 3,     /* workspace missing or too small */
+    ENGRAM_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+} engram_status;
+
+/* Bits OR-ed into the optional device error word. */
+#define ENGRAM_ERRBIT_TOKEN 0x1u  /* a token id outside [0, vocab) (used as pad) */
+#define ENGRAM_ERRBIT_HASH  0x2u  /* a computed hash id outside [0, num_embeddings) */
+#define ENGRAM_ERRBIT_ROW   0x4u  /* gather saw a row id outside [0, num_embeddings) */
+
+/* Geometry of one Engram layer ([block] constructor: ModelArgs dim, hc_mult,
+ * norm_eps; EngramLayout num_embeddings, head_dim, max_ngram_size, n_heads).
+ * Derived: n_hash_cols = (max_ngram_size - 1) * n_heads;
+ *          K = n_hash_cols * head_dim (wkv input width);
+ *          N = dim * (hc_mult + 1)     (wkv output width).
+ * Supported: dim % 8 == 0 and 8 <= dim <= 65536; 1 <= hc_mult <= 8;
+ * 2 <= max_ngram_size <= 16; n_heads >= 1 and n_hash_cols <= 1024;
+ * head_dim % 32 == 0 and 32 <= head_dim <= 1024; 1 <= num_embeddings < 2^31;
+ * vocab >= 1; norm_eps finite and >= 0. */
+typedef struct engram_geometry {
+    int32_t dim;             /* model width */
+    int32_t hc_mult;         /* hyper-connection streams */
+    int32_t max_ngram_size;  /* n-gram sizes 2..max_ngram_size */
+    int32_t n_heads;         /* hash heads per n-gram size */
+    int32_t head_dim;        /* table row width */
+    int32_t vocab;           /* raw token ids are in [0, vocab) */
+    int32_t pad_id;          /* compressed id used before position 0 */
+    int32_t reserved;        /* must be 0 */
+    int64_t num_embeddings;  /* table rows */
+    float norm_eps;          /* eps inside each rsqrt of the gate */
+    int32_t reserved2;       /* must be 0 */
+} engram_geometry;
+
+/* The hash tables, used exactly as given ([docs] EngramTables: token_map,
+ * multipliers, primes, offsets; never recomputed).  Device pointers. */
+typedef struct engram_hash_tables {
+    const int32_t* token_map;  /* [vocab] raw id -> compressed id */
+    const uint64_t* mult;      /* [n_hash_cols][max_ngram_size] per-lookback multipliers */
+    const uint64_t* prime;     /* [n_hash_cols] modulus of each column */
+    const uint64_t* offset;    /* [n_hash_cols] first table row of each column */
+} engram_hash_tables;
+
+const char* engram_status_string(engram_status s);
+
+/* Checks a geometry against the supported ranges above. */
+engram_status engram_check_geometry(const engram_geometry* g);
+
+/* Stage 1: the n-gram hash ([docs] stage 1 and NgramHashState; [block]
+ * forward's hash_ids argument).
+ *   ids      int32 [B, T]   raw token ids of T new positions per sequence.
+ *   state    int32 [B, max_ngram_size - 1] or NULL.  The compressed ids of the
+ *            last max_ngram_size-1 positions seen, oldest first; a fresh
+ *            sequence holds pad_id.  Read for the look-back before position 0
+ *            of this call, then overwritten with the last max_ngram_size-1
+ *            compressed ids (so prefill then decode equals one long prefill).
+ *            NULL = fresh pad history and no update.
+ *   hash_ids int32 [B, T, n_hash_cols] out.  Column col = (n-2)*n_heads + head
+ *            for n-gram size n:  c_j = token_map[ids] (compressed, unsigned
+ *            32-bit), mix = XOR_{k=0..n-1} c_{t-k} * mult[col][k] (mod 2^64),
+ *            hash = mix % prime[col] + offset[col]  (unsigned 64-bit).
+ *            A hash outside [0, num_embeddings) is written as -1 and flagged.
+ * Bit-exact (integer). */
+engram_status engram_hash(const engram_geometry* g, const engram_hash_tables* t,
+                          int32_t* state, const int32_t* ids, int32_t B, int32_t T,
+                          int32_t* hash_ids, uint32_t* err, void* stream);
+
+/* Stage 2: gather and dequantise table rows ([docs] stage 2, embed_rows,
+ * regen_table; [block] self.embed).
+ *   table    uint8 [num_embeddings, head_dim]      fp8 e4m3fn codes.
+ *   scales   uint8 [num_embeddings, head_dim / 32] e8m0 codes, one per 32-block.
+ *   hash_ids int32 [n_tok, n_hash_cols].
+ *   rows     bf16  [n_tok, n_hash_cols * head_dim] out: the fp32 product
+ *            e4m3(v) * 2^(s-127) rounded to bf16 (nearest-even; NaN -> 0x7FC0).
+ * Bit-exact. */
+engram_status engram_gather(const engram_geometry* g, const uint8_t* table,
+                            const uint8_t* scales, const int32_t* hash_ids, int64_t n_tok,
+                            uint16_t* rows, uint32_t* err, void* stream);
+
+/* Stage 3: the wkv projection ([docs] stage 3, linear_bf16; [block] self.wkv):
+ * kv[m][n] = bf16( sum_k a[m][k] * w[n][k] ), fp32 accumulation on bf16 MFMA,
+ * no bias.
+ *   a  bf16 [M, K];  w  bf16 [N, K] ([out, in]);  kv bf16 [M, N] out.
+ * Columns [s*dim, (s+1)*dim) of kv are the key of stream s; the last dim
+ * columns are the shared value. */
+engram_status engram_wkv(const engram_geometry* g, const uint16_t* a, const uint16_t* w,
+                         int64_t M, uint16_t* kv, void* stream);
+
+/* Stage 4: gate and add ([docs] gate_and_add; [block] forward after the
+ * projection; [gate] equations for a_k and g).  Per token and stream s:
+ *   w = q[s]*k[s];  rstd = rsqrt(mean(h^2)+eps) * rsqrt(mean(key^2)+eps);
+ *   a = sum(h*w*key) * rstd * dim^-0.5;
+ *   g = sigmoid(copysign(sqrt(max(|a|, 1e-6)), a)),  0 where mask is 0;
+ *   out = bf16(h + g*value); a masked position returns x bit-exactly.
+ *   x    bf16 [n_tok, hc_mult, dim];  kv bf16 [n_tok, dim*(hc_mult+1)];
+ *   q, k bf16 [hc_mult, dim];  mask uint8 [n_tok] or NULL (all live);
+ *   out  bf16 [n_tok, hc_mult, dim] (may be the same buffer as x);
+ *   gate fp32 [n_tok, hc_mult] or NULL.
+ * fp32 arithmetic with fixed-order reductions (run-to-run deterministic). */
+engram_status engram_gate_add(const engram_geometry* g, const uint16_t* x, const uint16_t* kv,
+                              const uint16_t* q, const uint16_t* k, const uint8_t* mask,
+                              int64_t n_tok, uint16_t* out, float* gate, void* stream);
+
+/* Bytes of workspace engram_forward needs for n_tok = B*T positions
+ * (hash ids, gathered rows and kv). */
+size_t engram_forward_workspace_size(const engram_geometry* g, int64_t n_tok);
+
+/* The whole forward ([block] Engram.forward with the hash in front):
+ * stage 1 -> 2 -> 3 -> 4 on one stream.  Arguments as in the stage calls;
+ * x, out: [B, T, hc_mult, dim]; ids, mask: [B, T]; gate: [B, T, hc_mult].
+ * workspace: device memory of at least engram_forward_workspace_size bytes,
+ * 256-byte aligned. */
+engram_status engram_forward(const engram_geometry* g, const engram_hash_tables* t,
+                             const uint8_t* table, const uint8_t* scales, const uint16_t* w,
+                             const uint16_t* q, const uint16_t* k, int32_t* state,
+                             const uint16_t* x, const int32_t* ids, const uint8_t* mask,
+                             int32_t B, int32_t T, uint16_t* out, float* gate,
+                             void* workspace, size_t workspace_bytes, uint32_t* err,
+                             void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ENGRAM_H */

@@ -1,0 +1,93 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the
+header declares, and rejects bad arguments on the host before touching the
+device (no compute call is made here)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import gram_memory_layer_amd as ge
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "engram.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(engram_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = ge.load()
+    names = header_functions()
+    assert {"engram_hash", "engram_gather", "engram_wkv", "engram_gate_add",
+            "engram_forward", "engram_forward_workspace_size"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def good():
+    return ge.Geometry.make(dim=5120, hc_mult=4, max_ngram_size=3, n_heads=12, head_dim=64,
+                            num_embeddings=25160950, vocab=129280)
+
+
+def test_geometry_checks():
+    assert ge.engram_check_geometry(good()) == 0
+    bad = [dict(dim=12), dict(dim=0), dict(hc_mult=0), dict(hc_mult=9), dict(head_dim=48),
+           dict(head_dim=16), dict(max_ngram_size=1), dict(max_ngram_size=17), dict(n_heads=0),
+           dict(num_embeddings=0), dict(num_embeddings=1 << 31), dict(n_heads=600)]
+    for kw in bad:
+        g = good()
+        for k, v in kw.items():
+            setattr(g, k, v)
+        assert ge.engram_check_geometry(g) != 0, kw
+    g = good()
+    g.norm_eps = float("nan")
+    assert ge.engram_check_geometry(g) == 1
+    g = good()
+    g.reserved = 1
+    assert ge.engram_check_geometry(g) == 1
+
+
+def test_derived_sizes():
+    g = good()
+    assert (g.n_hash_cols, g.K, g.N) == (24, 1536, 25600)
+    ws = ge.engram_forward_workspace_size(g, 4096)
+    assert ws == 4096 * 24 * 4 + 4096 * 1536 * 2 + 4096 * 25600 * 2
+    assert ge.engram_forward_workspace_size(g, 0) == 0
+
+
+def test_host_side_rejections_launch_nothing():
+    lib = ge.load()
+    g = good()
+    fake = C.c_void_p(1 << 20)           # never dereferenced: every call below fails validation
+    ht = ge.HashTables(fake, fake, fake, fake)
+    assert lib.engram_wkv(C.byref(g), None, fake, 16, fake, None) == 1
+    assert lib.engram_wkv(C.byref(g), fake, fake, -1, fake, None) == 1
+    assert lib.engram_wkv(C.byref(g), C.c_void_p((1 << 20) + 2), fake, 16, fake, None) == 1
+    assert lib.engram_gate_add(C.byref(g), fake, None, fake, fake, None, 4, fake, None, None) == 1
+    assert lib.engram_gather(C.byref(g), fake, fake, fake, -5, fake, None, None) == 1
+    assert lib.engram_hash(C.byref(g), None, None, fake, 1, 4, fake, None, None) == 1
+    assert lib.engram_hash(C.byref(g), C.byref(ht), None, fake, -1, 4, fake, None, None) == 1
+    # forward: workspace missing / too small / misaligned
+    args = [C.byref(g), C.byref(ht), fake, fake, fake, fake, fake, None, fake, fake, None, 1, 8,
+            fake, None]
+    assert lib.engram_forward(*args, None, 0, None, None) == 3
+    assert lib.engram_forward(*args, fake, 100, None, None) == 3
+    assert lib.engram_forward(*args, C.c_void_p((1 << 20) + 16), 1 << 30, None, None) == 3
+    # empty work is a no-op success
+    assert lib.engram_wkv(C.byref(g), fake, fake, 0, fake, None) == 0
+    assert lib.engram_hash(C.byref(g), C.byref(ht), None, fake, 0, 5, fake, None, None) == 0
+    # unsupported geometry is reported before anything else
+    g.head_dim = 40
+    assert lib.engram_wkv(C.byref(g), fake, fake, 16, fake, None) == 2
+    assert lib.engram_status_string(2) == b"unsupported geometry"
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    g = good()
+    with pytest.raises(ValueError):
+        ge.engram_wkv(g, torch.zeros(4, 1536, dtype=torch.bfloat16),
+                      torch.zeros(25600, 1536, dtype=torch.bfloat16))

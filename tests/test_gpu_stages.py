@@ -1,0 +1,290 @@
+"""GPU parity, stage by stage, at sizes the oracle finishes in seconds.
+
+Each stage gets the same input bytes on both sides (hash ids for the gather
+come from the oracle's hash, rows for the projection from the generator or
+the oracle), so each stage's rounding is isolated; the end-to-end forward is
+checked on top.  Bars: hash ids and gathered rows bit-exact; kv, gate and out
+per tests/tolerances.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import tolerances
+from tests.gpu_util import Workload, bits, device_tables, from_bits, geometry, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ge():
+    import gram_memory_layer_amd as ge
+    ge.load()
+    return ge
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def tiny(ge, dev):
+    return Workload(ge, "tiny", dev)
+
+
+# ------------------------------------------------------------------ stage 1: hash
+@pytest.mark.parametrize("B,T", [(1, 16), (4, 200), (3, 1), (2, 2), (5, 1000)])
+def test_hash_fresh_bit_exact(ge, dev, tiny, B, T):
+    say("hash fresh", B, T)
+    ids = synth.token_ids(tiny.cfg, B, T, name="h%d_%d" % (B, T))
+    ref = oracle.hash_ids(tiny.t, tiny.geom, oracle.HashState(B, T + 4), ids)
+    got = ge.engram_hash(tiny.g, tiny.tables, torch.from_numpy(ids).to(dev))
+    assert np.array_equal(got.cpu().numpy(), ref)
+
+
+def test_hash_state_carries_across_calls(ge, dev, tiny):
+    say("hash split")
+    B, T = 3, 40
+    ids = synth.token_ids(tiny.cfg, B, T, name="split")
+    ref = oracle.hash_ids(tiny.t, tiny.geom, oracle.HashState(B, T + 4), ids)
+    for k in (0, 1, 2, 5, 39):
+        state = torch.full((B, tiny.cfg.max_ngram_size - 1), tiny.cfg.pad_id, dtype=torch.int32,
+                           device=dev)
+        parts = []
+        if k:
+            parts.append(ge.engram_hash(tiny.g, tiny.tables, torch.from_numpy(ids[:, :k]).to(dev),
+                                        state=state))
+        for s in range(k, T):
+            parts.append(ge.engram_hash(tiny.g, tiny.tables,
+                                        torch.from_numpy(ids[:, s:s + 1].copy()).to(dev),
+                                        state=state))
+        got = torch.cat(parts, dim=1).cpu().numpy()
+        assert np.array_equal(got, ref), k
+        # the state holds the last n-1 compressed ids
+        assert np.array_equal(state.cpu().numpy(), tiny.t["token_map"][ids[:, -2:]])
+
+
+def test_hash_bad_token_flags_and_stays_in_range(ge, dev, tiny):
+    say("hash bad token")
+    ids = synth.token_ids(tiny.cfg, 1, 16, name="bad")
+    ids[0, 5] = tiny.cfg.vocab + 3
+    ids[0, 9] = -1
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    got = ge.engram_hash(tiny.g, tiny.tables, torch.from_numpy(ids).to(dev), err=err).cpu().numpy()
+    assert int(err.item()) & ge.ERRBIT_TOKEN
+    lo = tiny.t["offset"].astype(np.int64)
+    assert np.all(got >= lo) and np.all(got < lo + tiny.t["prime"].astype(np.int64))
+
+
+def test_hash_inconsistent_tables_flag(ge, dev, tiny):
+    say("hash bad table")
+    t = dict(tiny.t)
+    t["offset"] = t["offset"] + np.uint64(tiny.num_emb)      # every slot past the table
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    ids = torch.from_numpy(synth.token_ids(tiny.cfg, 1, 8)).to(dev)
+    got = ge.engram_hash(tiny.g, device_tables(t, dev), ids, err=err).cpu().numpy()
+    assert int(err.item()) & ge.ERRBIT_HASH
+    assert np.all(got == -1)
+
+
+# ------------------------------------------------------------------ stage 2: rows
+def test_gather_every_code_and_scale_pair(ge, dev):
+    say("gather exhaustive")
+    vc, sc = np.meshgrid(np.arange(256), np.arange(256), indexing="ij")
+    order = np.lexsort((vc.reshape(-1), sc.reshape(-1)))
+    table = vc.reshape(-1)[order].reshape(-1, 64).astype(np.uint8)
+    scales = sc.reshape(-1)[order].astype(np.uint8).reshape(-1, 32)[:, 0].reshape(-1, 2).copy()
+    rows = table.shape[0]
+    g = ge.Geometry.make(dim=64, hc_mult=1, max_ngram_size=2, n_heads=1, head_dim=64,
+                         num_embeddings=rows, vocab=1)
+    rng = np.random.default_rng(0)
+    ids = np.concatenate([np.arange(rows), rng.integers(0, rows, 333)]).astype(np.int32)[:, None]
+    ref = oracle.embed_rows(table, scales, ids[:, 0])
+    got = ge.engram_gather(g, torch.from_numpy(table).to(dev), torch.from_numpy(scales).to(dev),
+                           torch.from_numpy(ids).to(dev))
+    assert np.array_equal(bits(got).reshape(ref.shape), ref)
+
+
+def test_gather_tiny_bit_exact(ge, dev, tiny):
+    say("gather tiny")
+    ids = synth.token_ids(tiny.cfg, 2, 50, name="g")
+    hid = oracle.hash_ids(tiny.t, tiny.geom, oracle.HashState(2, 64), ids).reshape(100, -1)
+    ref = oracle.embed_rows(tiny.table.cpu().numpy(), tiny.scales.cpu().numpy(), hid)
+    got = ge.engram_gather(tiny.g, tiny.table, tiny.scales, torch.from_numpy(hid).to(dev))
+    assert np.array_equal(bits(got).reshape(ref.shape), ref)
+
+
+def test_gather_bad_id_gives_zero_row(ge, dev, tiny):
+    say("gather bad id")
+    hid = np.array([[0, 5, tiny.num_emb, -7]], np.int32)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    got = bits(ge.engram_gather(tiny.g, tiny.table, tiny.scales, torch.from_numpy(hid).to(dev),
+                                err=err)).reshape(4, -1)
+    assert int(err.item()) & ge.ERRBIT_ROW
+    assert np.all(got[2:] == 0)
+    ref = oracle.embed_rows(tiny.table.cpu().numpy(), tiny.scales.cpu().numpy(), hid[0, :2])
+    assert np.array_equal(got[:2], ref)
+
+
+# ------------------------------------------------------------------ stage 3: wkv
+def _abs_dot(a_bits, w_bits):
+    a = np.abs(tolerances.bf16_value(a_bits))
+    w = np.abs(tolerances.bf16_value(w_bits))
+    return a @ w.T
+
+
+def _wkv_case(ge, dev, g, M, seed, kind="randn"):
+    gen = torch.Generator(device=dev).manual_seed(seed)
+    if kind == "randn":
+        a = torch.randn((M, g.K), generator=gen, device=dev).to(torch.bfloat16)
+        w = (torch.randn((g.N, g.K), generator=gen, device=dev) * g.K ** -0.5).to(torch.bfloat16)
+    else:  # small integers: every partial sum exact in fp32
+        a = torch.randint(-8, 9, (M, g.K), generator=gen, device=dev).to(torch.bfloat16)
+        w = torch.randint(-8, 9, (g.N, g.K), generator=gen, device=dev).to(torch.bfloat16)
+    kv = ge.engram_wkv(g, a, w)
+    ab, wb = bits(a), bits(w)
+    ref = oracle.linear(ab, wb)
+    return bits(kv), ref, ab, wb
+
+
+@pytest.mark.parametrize("M", [1, 16, 63, 64, 65, 300, 1024, 1100])
+def test_wkv_tiny_geometry(ge, dev, tiny, M):
+    say("wkv tiny M", M)
+    kv, ref, ab, wb = _wkv_case(ge, dev, tiny.g, M, seed=M)
+    st = tolerances.check_kv(kv, ref, _abs_dot(ab, wb), tiny.g.K)
+    say("  ", st)
+
+
+@pytest.mark.parametrize("M", [7, 300, 1500])
+def test_wkv_ragged_n_and_k(ge, dev, M):
+    # N = 200*5 = 1000 (not a multiple of any tile), K = 5*32 = 160 (a half k-tile)
+    g = ge.Geometry.make(dim=200, hc_mult=4, max_ngram_size=6, n_heads=1, head_dim=32,
+                         num_embeddings=1, vocab=1)
+    say("wkv ragged M", M, "N", g.N, "K", g.K)
+    kv, ref, ab, wb = _wkv_case(ge, dev, g, M, seed=100 + M)
+    tolerances.check_kv(kv, ref, _abs_dot(ab, wb), g.K)
+
+
+@pytest.mark.parametrize("M", [50, 1030])
+def test_wkv_small_integers_exact(ge, dev, tiny, M):
+    say("wkv small ints", M)
+    kv, ref, _, _ = _wkv_case(ge, dev, tiny.g, M, seed=7, kind="int")
+    assert np.array_equal(kv, ref)
+
+
+@pytest.mark.parametrize("M", [128, 1280])
+def test_wkv_one_hot_rows_are_weight_columns(ge, dev, tiny, M):
+    say("wkv one-hot", M)
+    K = tiny.g.K
+    a = torch.zeros((M, K), dtype=torch.bfloat16, device=dev)
+    r = torch.arange(M, device=dev)
+    a[r, r % K] = 1.0
+    w = synth.wkv_weight(tiny.cfg, dev)
+    kv = ge.engram_wkv(tiny.g, a, w)
+    expect = w.t()[(r % K)]
+    assert torch.equal(kv.view(torch.int16), expect.contiguous().view(torch.int16))
+
+
+# ------------------------------------------------------------------ stage 4: gate
+def _gate_inputs(cfg, n_tok, dev, name="kvg"):
+    x = synth.activations(cfg, n_tok, dev, name="x" + name)
+    q, k = synth.qk_weights(cfg, dev)
+    kv, cat = synth.gate_stress_kv(cfg, x, q, k, name=name)
+    return x, kv, q, k, cat
+
+
+def _gate_check(ge, g, x, kv, q, k, mask=None, inplace=False):
+    n_tok = x.shape[0]
+    gate = torch.empty((n_tok, g.hc_mult), dtype=torch.float32, device=x.device)
+    xb = bits(x)
+    if inplace:
+        out = x.clone()
+        ge.engram_gate_add(g, out, kv, q, k, mask=mask, out=out, gate=gate)
+    else:
+        out = ge.engram_gate_add(g, x, kv, q, k, mask=mask, gate=gate)
+    m = None if mask is None else mask.cpu().numpy()
+    ref_out, ref_g, ref_a = oracle.gate_and_add(xb, bits(kv), bits(q), bits(k), g.norm_eps, m)
+    gs = tolerances.check_gate(gate.cpu().numpy(), ref_g, ref_a)
+    os_ = tolerances.check_out(bits(out), ref_out, xb, bits(kv)[:, g.hc_mult * g.dim:],
+                               gate.cpu().numpy(), ref_g)
+    if m is not None:
+        assert np.array_equal(bits(out)[~m.astype(bool)], xb[~m.astype(bool)])
+    return gs, os_, out, gate
+
+
+def test_gate_tiny(ge, dev, tiny):
+    say("gate tiny")
+    x, kv, q, k, _ = _gate_inputs(tiny.cfg, 64, dev)
+    say("  ", _gate_check(ge, tiny.g, x, kv, q, k)[:2])
+
+
+def test_gate_full_width_stress_recipe(ge, dev):
+    cfg = synth.config("gate_stress")
+    t = synth.hash_tables(cfg)
+    g = geometry(ge, cfg, t["num_embeddings"])
+    say("gate dim 5120, 96 tokens")
+    x, kv, q, k, cat = _gate_inputs(cfg, 96, dev)
+    gs, os_, out, gate = _gate_check(ge, g, x, kv, q, k)
+    say("  ", gs, os_)
+    # exactly orthogonal keys: dot is +0 -> g = sigmoid(+sqrt(fp32(1e-6)))
+    orth = cat.cpu().numpy() == 0
+    assert orth.any()
+    g0 = np.float32(1.0 / (1.0 + np.exp(-np.sqrt(np.float64(np.float32(1e-6))))))
+    gv = gate.cpu().numpy()[orth]
+    assert np.all(np.abs(gv - g0) <= np.spacing(g0)), gv[:4]
+
+
+def test_gate_mask_and_in_place(ge, dev, tiny):
+    say("gate mask in place")
+    x, kv, q, k, _ = _gate_inputs(tiny.cfg, 40, dev, name="m")
+    mask = torch.ones(40, dtype=torch.bool, device=dev)
+    mask[[0, 3, 4, 39]] = False
+    _, _, out, gate = _gate_check(ge, tiny.g, x, kv, q, k, mask=mask, inplace=True)
+    assert torch.all(gate[~mask] == 0)
+
+
+def test_gate_deterministic(ge, dev):
+    cfg = synth.config("prefill")
+    g = geometry(ge, cfg, 1)
+    say("gate determinism")
+    x, kv, q, k, _ = _gate_inputs(cfg, 128, dev, name="d")
+    g1 = torch.empty((128, 4), device=dev)
+    g2 = torch.empty((128, 4), device=dev)
+    o1 = ge.engram_gate_add(g, x, kv, q, k, gate=g1)
+    o2 = ge.engram_gate_add(g, x, kv, q, k, gate=g2)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(g1, g2)
+
+
+# ------------------------------------------------------------------ end to end
+def test_forward_tiny_end_to_end(ge, dev, tiny):
+    say("forward tiny")
+    cfg = tiny.cfg
+    for B, T in ((1, 16), (3, 37)):
+        ids = synth.token_ids(cfg, B, T, name="f%d" % T)
+        x = synth.activations(cfg, B * T, dev, name="xf%d" % T).reshape(B, T, cfg.hc_mult, cfg.dim)
+        mask = torch.from_numpy(synth.token_ids(cfg, B, T, name="mk") % 5 != 0).to(dev)
+        gate = torch.empty((B, T, cfg.hc_mult), dtype=torch.float32, device=dev)
+        state = torch.full((B, cfg.max_ngram_size - 1), cfg.pad_id, dtype=torch.int32, device=dev)
+        out = ge.engram_forward(tiny.g, tiny.tables, tiny.table, tiny.scales, tiny.w, tiny.q,
+                                tiny.k, x, torch.from_numpy(ids).to(dev), mask=mask, state=state,
+                                gate=gate)
+        ref = oracle.forward(tiny.t, tiny.geom, oracle.HashState(B, T + 4), ids,
+                             tiny.table.cpu().numpy(), tiny.scales.cpu().numpy(), bits(tiny.w),
+                             bits(tiny.q), bits(tiny.k), bits(x), mask.cpu().numpy())
+        n = B * T
+        hd = cfg.hc_mult * cfg.dim
+        da = tolerances.key_ulp_da(bits(x).reshape(n, cfg.hc_mult, cfg.dim),
+                                   ref["kv"][:, :hd].reshape(n, cfg.hc_mult, cfg.dim),
+                                   bits(tiny.q), bits(tiny.k), cfg.norm_eps)
+        tolerances.check_gate(gate.cpu().numpy().reshape(n, -1), ref["gate"], ref["a"], da=da)
+        tolerances.check_out(bits(out).reshape(n, cfg.hc_mult, cfg.dim), ref["out"],
+                             bits(x).reshape(n, cfg.hc_mult, cfg.dim),
+                             ref["kv"][:, cfg.hc_mult * cfg.dim:],
+                             gate.cpu().numpy().reshape(n, -1), ref["gate"], v_ulps=1)
+        mk = mask.cpu().numpy().reshape(-1)
+        assert np.array_equal(bits(out).reshape(n, -1)[~mk], bits(x).reshape(n, -1)[~mk])
+        assert np.array_equal(state.cpu().numpy(), tiny.t["token_map"][ids[:, -2:]])
