@@ -4,8 +4,9 @@
 // bf16 MFMA GEMM for gfx950.  Both operands are K-contiguous ([M, K] and
 // [N, K]), which is exactly the per-lane operand layout of
 // v_mfma_f32_32x32x16_bf16 (each lane holds 8 consecutive k of one row), so
-// tiles go global -> registers -> LDS unchanged and come back out of LDS as
-// one 16-byte read per fragment.
+// tiles go to LDS unchanged and come back out as one 16-byte read per
+// fragment.  Two kernels: the main one (M >= 1024, K % 64 == 0, further
+// below) and a general one for small M or ragged K (right here).
 //
 //  * Macro tile BM x BN x 64, double-buffered in LDS; the next k-tile's global
 //    loads are issued before the current tile's MFMAs.
@@ -18,6 +19,8 @@
 //    groups of 4 M-tiles, share A and W panels in that XCD's L2.
 //  * Edges (M, N, K not multiples of the tile) are zero-filled on load and
 //    masked on store; no access leaves the operands.
+#include <type_traits>
+
 #include "internal.h"
 
 namespace engram {
@@ -174,6 +177,222 @@ wkv_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, int64
     }
 }
 
+// ---------------------------------------------------------------------------
+// Main kernel for K % 64 == 0: 256 x 256 output tiles, 4 waves of 128 x 128,
+// k-tiles of 64 double-buffered in LDS (2 x 64 KiB).
+//
+// Tiles move global -> LDS with buffer_load_dwordx4 ... lds (no register
+// staging): one instruction writes 1 KiB = 8 LDS rows of 128 bytes, lane l
+// landing at byte 16*l, so lane l fetches the logical 16-byte chunk that the
+// swizzle places at that slot.  Rows past M (or N) lie past the buffer
+// descriptor's extent and read as zero.  While k-tile kt is multiplied the
+// loads of k-tile kt+1 are in flight; one barrier per k-tile hands the next
+// stage over.  (Touching k-tile kt+2 into L2 one tile early, or a 4-stage
+// ring of 32-wide k-tiles, measured slower on this shape.)  Within a k-tile the
+// fragments of the next 16-wide k-step are read from LDS while the current
+// k-step's 16 MFMAs issue.
+constexpr int F_BM = 256, F_BN = 256, F_WM = 128, F_WN = 128, F_NT = 256;
+constexpr int F_STAGE = (F_BM + F_BN) * 128;  // bytes per LDS stage
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    // raw buffer: stride 0, num_records = bytes; word 3 = 0x00020000 for gfx9 data format
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// 16-byte slot of logical chunk c (0..7) in a 128-byte LDS row: XOR with a
+// row function that is a permutation on any 8 consecutive rows and maps the
+// even and the odd rows of any 16 consecutive rows onto all 8 slots, so a
+// fragment read (32 consecutive rows, one logical chunk) is free of bank
+// conflicts for both 8- and 16-lane LDS issue groups.
+__device__ __forceinline__ int slot128(int row, int c) {
+    return c ^ ((row & 7) ^ ((row >> 3) & 1));
+}
+
+__global__ void __launch_bounds__(F_NT, 1)
+wkv_fast_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, int64_t M, int N,
+                int K, uint16_t* __restrict__ C, int tiles_m, int tiles_n, int per_xcd) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * F_STAGE];
+
+    const int b = blockIdx.x;
+    const int L = (b % N_XCD) * per_xcd + b / N_XCD;
+    if (L >= tiles_m * tiles_n) return;
+    const int group_size = GROUP_M * tiles_n;
+    const int first_m = (L / group_size) * GROUP_M;
+    const int gm = min(tiles_m - first_m, GROUP_M);
+    const int mt = first_m + (L % group_size) % gm;
+    const int nt = (L % group_size) / gm;
+    const int64_t m0 = (int64_t)mt * F_BM;
+    const int n0 = nt * F_BN;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    const int64_t rows_a = min((int64_t)F_BM, M - m0);
+    const int rows_w = min(F_BN, N - n0);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + m0 * K, (uint32_t)(rows_a * K * 2));
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (int64_t)n0 * K, (uint32_t)(rows_w * K * 2));
+
+    // load slots: instruction i (0..7) of this wave fills LDS segment
+    // seg = 4*i + wave = rows 8*seg .. 8*seg+7 of the A rows (then the W rows)
+    uint32_t voff[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = (4 * i + wave) * 8 + (lane >> 3);
+        voff[i] = (uint32_t)(row * K * 2 + slot128(row, lane & 7) * 16);
+    }
+    auto issue_loads = [&](int kt, int stage) {
+        uint8_t* st = smem + stage * F_STAGE;
+        const int soff = kt * 128;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ra, (lds_void*)(st + (4 * i + wave) * 1024), 16, voff[i], soff, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rw, (lds_void*)(st + F_BM * 128 + (4 * i + wave) * 1024), 16, voff[i], soff, 0, 0);
+    };
+
+    const int lrow = lane & 31, lhalf = lane >> 5;
+    bf16x8 fa[2][4], fw[2][4];
+    auto read_frags = [&](int stage, int ks, int buf) {
+        const uint8_t* st = smem + stage * F_STAGE;
+        const int c = ks * 2 + lhalf;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = wm * F_WM + i * 32 + lrow;
+            fa[buf][i] = *reinterpret_cast<const bf16x8*>(st + row * 128 + slot128(row, c) * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = wn * F_WN + j * 32 + lrow;
+            fw[buf][j] = *reinterpret_cast<const bf16x8*>(st + F_BM * 128 + row * 128 +
+                                                          slot128(row, c) * 16);
+        }
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
+
+    auto mfma_half = [&](int cur, int j0) {
+#pragma unroll
+        for (int j = j0; j < j0 + 2; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[cur][j], fa[cur][i],
+                                                                    acc[j][i], 0, 0, 0);
+    };
+    // One k-tile = 4 k-steps of 16 MFMAs, each k-step its own scheduling
+    // region (sched_barrier fences stop the compiler from regrouping MFMAs by
+    // accumulator across k-steps, which would chain dependent MFMAs).  The
+    // next k-step's 8 fragment reads are interleaved with the current MFMAs;
+    // the next k-tile's 16 LDS-bound buffer loads go out during k-step 0.  The
+    // last k-step is split around the barrier so that the next k-tile's first
+    // fragment reads overlap its second half.
+    //   LOADS: k-tile kt+1 exists (its loads are issued here)
+    auto k_tile = [&](int kt, auto with_loads) {
+        constexpr bool LOADS = decltype(with_loads)::value;
+        const int stage = kt & 1;
+#pragma unroll
+        for (int ks = 0; ks < 3; ++ks) {
+            const int cur = ks & 1;
+            if (LOADS && ks == 0) issue_loads(kt + 1, stage ^ 1);
+            read_frags(stage, ks + 1, cur ^ 1);
+            mfma_half(cur, 0);
+            mfma_half(cur, 2);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                if (LOADS && ks == 0) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        mfma_half(1, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (LOADS) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads landed
+            __syncthreads();  // everyone's loads landed; tile kt fully consumed
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(stage ^ 1, 0, 0);
+        }
+        mfma_half(1, 2);
+        if constexpr (LOADS) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    using T = std::true_type;
+    using F = std::false_type;
+
+    const int nk = K / BK;
+    issue_loads(0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    read_frags(0, 0, 0);
+    for (int kt = 0; kt + 1 < nk; ++kt) k_tile(kt, T{});
+    k_tile(nk - 1, F{});
+    __syncthreads();  // every wave is done with the operand stages
+
+    // ---- epilogue through LDS.  D[n][m]: lane holds m = lane%32 (+32 i) and
+    // n = 32 j + 8 (v/4) + 4 (lane/32) + v%4.  Each wave writes its 128 x 128
+    // block as bf16 rows [m][n] into its own 32 KiB of LDS (16-byte chunks
+    // XOR-swizzled by row), then reads it back so that 16 lanes store one
+    // 256-byte row run with 16-byte stores.
+    uint8_t* ep = smem + wave * (128 * 256);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int r = i * 32 + lrow;
+                const int nn = j * 32 + 8 * g4 + 4 * lhalf;  // multiple of 4
+                const int ch = (nn >> 3) ^ (r & 15);
+                const uint32_t lo = f32_to_bf16(acc[j][i][4 * g4 + 0]) |
+                                    (f32_to_bf16(acc[j][i][4 * g4 + 1]) << 16);
+                const uint32_t hi = f32_to_bf16(acc[j][i][4 * g4 + 2]) |
+                                    (f32_to_bf16(acc[j][i][4 * g4 + 3]) << 16);
+                *reinterpret_cast<uint2*>(ep + r * 256 + ch * 16 + (nn & 4) * 2) =
+                    make_uint2(lo, hi);
+            }
+    const int rsub = lane >> 4, csub = lane & 15;
+#pragma unroll 4
+    for (int it = 0; it < 32; ++it) {
+        const int r = it * 4 + rsub;
+        const uint4 v = *reinterpret_cast<const uint4*>(ep + r * 256 + ((csub ^ (r & 15)) << 4));
+        const int64_t m = m0 + wm * F_WM + r;
+        const int n = n0 + wn * F_WN + csub * 8;
+        if (m < M && n < N) *reinterpret_cast<uint4*>(C + m * N + n) = v;
+    }
+}
+
+hipError_t run_fast(const uint16_t* a, const uint16_t* w, int64_t M, int N, int K, uint16_t* kv,
+                    hipStream_t s) {
+    const int tiles_m = (int)((M + F_BM - 1) / F_BM);
+    const int tiles_n = (N + F_BN - 1) / F_BN;
+    const int total = tiles_m * tiles_n;
+    const int per_xcd = (total + N_XCD - 1) / N_XCD;
+    wkv_fast_kernel<<<dim3(per_xcd * N_XCD), dim3(F_NT), 0, s>>>(a, w, M, N, K, kv, tiles_m,
+                                                                 tiles_n, per_xcd);
+    return hipGetLastError();
+}
+
 template <int BM, int BN, int WM, int WN>
 hipError_t run(const uint16_t* a, const uint16_t* w, int64_t M, int N, int K, uint16_t* kv,
                hipStream_t s) {
@@ -192,6 +411,8 @@ hipError_t run(const uint16_t* a, const uint16_t* w, int64_t M, int N, int K, ui
 hipError_t launch_wkv(const uint16_t* a, const uint16_t* w, int64_t M, int N, int K,
                       uint16_t* kv, hipStream_t s) {
     if (M == 0) return hipSuccess;
+    if (M >= 1024 && K % BK == 0 && (int64_t)K * 2 * F_BM < (1ll << 31))
+        return run_fast(a, w, M, N, K, kv, s);
     if (M >= 1024) return run<256, 256, 128, 128>(a, w, M, N, K, kv, s);
     return run<64, 64, 32, 32>(a, w, M, N, K, kv, s);
 }

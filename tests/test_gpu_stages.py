@@ -168,6 +168,16 @@ def test_wkv_ragged_n_and_k(ge, dev, M):
     tolerances.check_kv(kv, ref, _abs_dot(ab, wb), g.K)
 
 
+@pytest.mark.parametrize("M", [1030, 2600])
+def test_wkv_ragged_n_main_kernel(ge, dev, M):
+    # K = 2*32 = 64 (a whole k-tile), N = 1000: large-M kernel with a ragged N and M edge
+    g = ge.Geometry.make(dim=200, hc_mult=4, max_ngram_size=3, n_heads=1, head_dim=32,
+                         num_embeddings=1, vocab=1)
+    say("wkv ragged main M", M, "N", g.N, "K", g.K)
+    kv, ref, ab, wb = _wkv_case(ge, dev, g, M, seed=200 + M)
+    tolerances.check_kv(kv, ref, _abs_dot(ab, wb), g.K)
+
+
 @pytest.mark.parametrize("M", [50, 1030])
 def test_wkv_small_integers_exact(ge, dev, tiny, M):
     say("wkv small ints", M)
