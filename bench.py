@@ -36,6 +36,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=2048, help="tokens the oracle runs")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run 3 plain device copies of exactly 1 GiB (a known-size kernel "
+                        "against which HBM byte counters are scaled)")
     return p.parse_args()
 
 
@@ -161,6 +164,16 @@ def main():
                      "unit": "GB/s", "frac": round(gate_bytes / st_gate / 1e9 / PEAK_HBM_GBS, 4)},
         "wall_s": round(wall, 3),
     }
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        rec["copy_calibration_bytes"] = 1 << 30
+        del src, dst
 
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(cfg, t, table, scales, w, q, k, x, ids_np, mask,

@@ -56,7 +56,7 @@ const char* engram_status_string(engram_status s) {
 engram_status engram_check_geometry(const engram_geometry* g) {
     if (g == nullptr) return ENGRAM_ERR_INVALID_ARG;
     if (g->reserved != 0 || g->reserved2 != 0) return ENGRAM_ERR_INVALID_ARG;
-    if (g->dim < 8 || g->dim > 65536 || g->dim % 8 != 0) return ENGRAM_ERR_UNSUPPORTED;
+    if (g->dim < 8 || g->dim > 32768 || g->dim % 8 != 0) return ENGRAM_ERR_UNSUPPORTED;
     if (g->hc_mult < 1 || g->hc_mult > 8) return ENGRAM_ERR_UNSUPPORTED;
     if (g->max_ngram_size < 2 || g->max_ngram_size > 16) return ENGRAM_ERR_UNSUPPORTED;
     if (g->n_heads < 1 || (int64_t)(g->max_ngram_size - 1) * g->n_heads > 1024)

@@ -8,7 +8,10 @@
 //   S_hh[s] = sum h^2,  S_kk[s] = sum key^2,  S_hwk[s] = sum (h*w)*key,
 // and after a fixed-order block reduction writes out = bf16(h + g[s]*v) from
 // the registers it already holds.  HBM traffic is the algorithmic minimum:
-// x and kv read once, out written once (q and k are L2-resident).
+// x and kv read once, out written once (nontemporal); q and k are
+// L2-resident.  (Persistent workgroups holding q and k in registers, DPP
+// reductions with one barrier per token, and fewer threads with more chunks
+// each all measured slower on the T=4096 prefill shape.)
 //
 // x and out may be the same buffer: every thread writes only the chunks it
 // has itself read, after reading them (so neither pointer is __restrict__).
@@ -25,6 +28,14 @@ namespace {
 
 __device__ __forceinline__ float lo_f(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float hi_f(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// write-once output: 16-byte store with the nontemporal hint
+__device__ __forceinline__ void st_nt(uint16_t* p, uint4 v) {
+    const u32x4 u = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(u, reinterpret_cast<u32x4*>(p));
+}
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -53,7 +64,11 @@ __global__ void __launch_bounds__(1024) gate_kernel(
     uint16_t* ot = out + tok * HC * dim;
     const bool live = (mask == nullptr) || (mask[tok] != 0);
 
-    uint4 xr[HC][NCH];
+    // KEEP: x and the value stay in registers from the loads to the output
+    // pass; for wide geometries (HC * NCH > 8) they are re-read instead.
+    constexpr bool KEEP = HC * NCH <= 8;
+    constexpr int KC = KEEP ? NCH : 1;
+    uint4 xr[HC][KC];
     if (!live) {
         // masked position: the gate is 0 and x passes through unchanged
 #pragma unroll
@@ -62,8 +77,8 @@ __global__ void __launch_bounds__(1024) gate_kernel(
             if (c < d8)
 #pragma unroll
                 for (int s = 0; s < HC; ++s) {
-                    const uint4 u = *reinterpret_cast<const uint4*>(xt + (int64_t)s * dim + c * 8);
-                    *reinterpret_cast<uint4*>(ot + (int64_t)s * dim + c * 8) = u;
+                    st_nt(ot + (int64_t)s * dim + c * 8,
+                          *reinterpret_cast<const uint4*>(xt + (int64_t)s * dim + c * 8));
                 }
         }
         if (gate && tid < HC) gate[tok * HC + tid] = 0.0f;
@@ -73,19 +88,19 @@ __global__ void __launch_bounds__(1024) gate_kernel(
     float acc[NS];
 #pragma unroll
     for (int j = 0; j < NS; ++j) acc[j] = 0.0f;
-    uint4 vr[NCH];
+    uint4 vr[KC];
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
         const int c = tid + i * nthr;
         if (c < d8) {
-            vr[i] = *reinterpret_cast<const uint4*>(kvt + (int64_t)HC * dim + c * 8);
+            if (KEEP) vr[i < KC ? i : 0] = *reinterpret_cast<const uint4*>(kvt + (int64_t)HC * dim + c * 8);
 #pragma unroll
             for (int s = 0; s < HC; ++s) {
                 const uint4 h = *reinterpret_cast<const uint4*>(xt + (int64_t)s * dim + c * 8);
                 const uint4 key = *reinterpret_cast<const uint4*>(kvt + (int64_t)s * dim + c * 8);
                 const uint4 qq = *reinterpret_cast<const uint4*>(q + (int64_t)s * dim + c * 8);
                 const uint4 kk = *reinterpret_cast<const uint4*>(kw + (int64_t)s * dim + c * 8);
-                xr[s][i] = h;
+                if (KEEP) xr[s][i < KC ? i : 0] = h;
                 const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
                 const uint32_t kyw[4] = {key.x, key.y, key.z, key.w};
                 const uint32_t qw[4] = {qq.x, qq.y, qq.z, qq.w};
@@ -142,10 +157,14 @@ __global__ void __launch_bounds__(1024) gate_kernel(
     for (int i = 0; i < NCH; ++i) {
         const int c = tid + i * nthr;
         if (c < d8) {
-            const uint32_t vw[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+            const uint4 vv = KEEP ? vr[i < KC ? i : 0]
+                                  : *reinterpret_cast<const uint4*>(kvt + (int64_t)HC * dim + c * 8);
+            const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
             for (int s = 0; s < HC; ++s) {
-                const uint32_t hw[4] = {xr[s][i].x, xr[s][i].y, xr[s][i].z, xr[s][i].w};
+                const uint4 hh = KEEP ? xr[s][i < KC ? i : 0]
+                                      : *reinterpret_cast<const uint4*>(xt + (int64_t)s * dim + c * 8);
+                const uint32_t hw[4] = {hh.x, hh.y, hh.z, hh.w};
                 uint32_t o[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -153,8 +172,7 @@ __global__ void __launch_bounds__(1024) gate_kernel(
                     const float r1 = __fmaf_rn(g[s], hi_f(vw[e]), hi_f(hw[e]));
                     o[e] = f32_to_bf16(r0) | (f32_to_bf16(r1) << 16);
                 }
-                *reinterpret_cast<uint4*>(ot + (int64_t)s * dim + c * 8) =
-                    make_uint4(o[0], o[1], o[2], o[3]);
+                st_nt(ot + (int64_t)s * dim + c * 8, make_uint4(o[0], o[1], o[2], o[3]));
             }
         }
     }
@@ -165,8 +183,10 @@ hipError_t run_hc(const Geom& g, const uint16_t* x, const uint16_t* kv, const ui
                   const uint16_t* k, const uint8_t* mask, int64_t n_tok, uint16_t* out,
                   float* gate, hipStream_t s) {
     const int d8 = g.dim / 8;
+    // one 16-byte chunk per thread and stream up to 1024 threads (640 at
+    // dim 5120): measured faster than fewer threads holding more chunks
     int nch = 1;
-    while (nch < 8 && (d8 + nch - 1) / nch > 512) nch *= 2;
+    while (nch < 4 && (d8 + nch - 1) / nch > 1024) nch *= 2;  // dim <= 32768
     int threads = (d8 + nch - 1) / nch;
     threads = (threads + 63) / 64 * 64;
     const float inv_sqrt_dim = (float)(1.0 / sqrt((double)g.dim));
@@ -180,7 +200,6 @@ hipError_t run_hc(const Geom& g, const uint16_t* x, const uint16_t* kv, const ui
         ENGRAM_GATE_CASE(1)
         ENGRAM_GATE_CASE(2)
         ENGRAM_GATE_CASE(4)
-        ENGRAM_GATE_CASE(8)
         default: return hipErrorInvalidValue;
     }
 #undef ENGRAM_GATE_CASE

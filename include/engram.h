@@ -50,7 +50,7 @@ typedef enum engram_status {
  * Derived: n_hash_cols = (max_ngram_size - 1) * n_heads;
  *          K = n_hash_cols * head_dim (wkv input width);
  *          N = dim * (hc_mult + 1)     (wkv output width).
- * Supported: dim % 8 == 0 and 8 <= dim <= 65536; 1 <= hc_mult <= 8;
+ * Supported: dim % 8 == 0 and 8 <= dim <= 32768; 1 <= hc_mult <= 8;
  * 2 <= max_ngram_size <= 16; n_heads >= 1 and n_hash_cols <= 1024;
  * head_dim % 32 == 0 and 32 <= head_dim <= 1024; 1 <= num_embeddings < 2^31;
  * vocab >= 1; norm_eps finite and >= 0. */

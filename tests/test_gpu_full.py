@@ -1,0 +1,240 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times.
+
+Integer stages are compared everywhere (hash ids for every position, the row
+gather for every position); floating-point outputs on sampled positions that
+the oracle computes one by one (sampled rows of the projection, sampled
+tokens end to end), plus properties that hold at any size (masked positions
+return x bit-exactly, exactly orthogonal keys give sigmoid(+sqrt(1e-6))).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import tolerances
+from tests.gpu_util import Workload, bits, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ge():
+    import gram_memory_layer_amd as ge
+    ge.load()
+    return ge
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return torch.device("cuda:0")
+
+
+def _sample_positions(T, extra=(), n=16, seed=0):
+    rng = np.random.default_rng(seed)
+    pos = set([0, 1, 2, T - 1] + list(extra))
+    pos.update(rng.integers(0, T, n).tolist())
+    return np.array(sorted(p for p in pos if 0 <= p < T))
+
+
+def _oracle_tokens(wl, ids_row, positions, x_bits, mask_bits=None):
+    """Oracle forward for chosen positions of one sequence: hash over the
+    sequence prefix, rows of those positions, projection, gate."""
+    cfg = wl.cfg
+    hid = oracle.hash_ids(wl.t, wl.geom, oracle.HashState(1, len(ids_row) + 4), ids_row[None])[0]
+    h = hid[positions]
+    tab, sc, inv = wl.host_rows(h)
+    rows = oracle.embed_rows(tab, sc, inv.reshape(-1)).reshape(len(positions), -1)
+    kv = oracle.linear(rows, bits(wl.w))
+    out, gate, a = oracle.gate_and_add(x_bits, kv, bits(wl.q), bits(wl.k), cfg.norm_eps, mask_bits)
+    return dict(hash_ids=hid, rows=rows, kv=kv, out=out, gate=gate, a=a)
+
+
+def _check_tokens(ref, out_bits, gate_gpu, x_bits, cfg):
+    hd = cfg.hc_mult * cfg.dim
+    n = x_bits.shape[0]
+    da = tolerances.key_ulp_da(x_bits, ref["kv"][:, :hd].reshape(n, cfg.hc_mult, cfg.dim),
+                               bits_q(ref), bits_k(ref), cfg.norm_eps)
+    gs = tolerances.check_gate(gate_gpu, ref["gate"], ref["a"], da=da)
+    os_ = tolerances.check_out(out_bits, ref["out"], x_bits, ref["kv"][:, hd:], gate_gpu,
+                               ref["gate"], v_ulps=1)
+    return gs, os_
+
+
+def bits_q(ref):
+    return ref["_q"]
+
+
+def bits_k(ref):
+    return ref["_k"]
+
+
+# ------------------------------------------------------------------ T=4096 prefill
+def test_prefill_full(ge, dev):
+    say("prefill full: building 25.16M-row table")
+    wl = Workload(ge, "prefill", dev)
+    cfg = wl.cfg
+    B, T = cfg.B, cfg.T
+    ids_np = synth.token_ids(cfg, B, T)
+    ids = torch.from_numpy(ids_np).to(dev)
+    x = synth.activations(cfg, B * T, dev).reshape(B, T, cfg.hc_mult, cfg.dim)
+    state = torch.full((B, cfg.max_ngram_size - 1), cfg.pad_id, dtype=torch.int32, device=dev)
+    gate = torch.empty((B, T, cfg.hc_mult), dtype=torch.float32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    layer = ge.EngramLayer(wl.g, wl.tables, wl.table, wl.scales, wl.w, wl.q, wl.k)
+    out = layer.forward(x, ids, state=state, gate=gate, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    say("prefill full: hash and gather for every position")
+    ref_hid = oracle.hash_ids(wl.t, wl.geom, oracle.HashState(B, T + 4), ids_np)
+    hid = ge.engram_hash(wl.g, wl.tables, ids)
+    assert np.array_equal(hid.cpu().numpy(), ref_hid)
+    assert np.array_equal(state.cpu().numpy(), wl.t["token_map"][ids_np[:, -2:]])
+    tab, sc, inv = wl.host_rows(ref_hid)
+    ref_rows = oracle.embed_rows(tab, sc, inv.reshape(-1)).reshape(B * T, -1)
+    rows = ge.engram_gather(wl.g, wl.table, wl.scales, torch.from_numpy(ref_hid).to(dev))
+    assert np.array_equal(bits(rows).reshape(ref_rows.shape), ref_rows)
+
+    say("prefill full: projection, sampled rows of the full M=4096 launch")
+    kv = ge.engram_wkv(wl.g, rows, wl.w)
+    pos = _sample_positions(T, n=12, seed=1)
+    ref_kv = oracle.linear(ref_rows[pos], bits(wl.w))
+    absdot = np.abs(tolerances.bf16_value(ref_rows[pos])) @ np.abs(tolerances.bf16_value(bits(wl.w))).T
+    st = tolerances.check_kv(bits(kv[torch.from_numpy(pos).to(dev)]), ref_kv, absdot, wl.g.K)
+    say("   kv", st)
+
+    say("prefill full: end to end on sampled positions")
+    xb = bits(x).reshape(B * T, cfg.hc_mult, cfg.dim)
+    ref = _oracle_tokens(wl, ids_np[0], pos, xb[pos])
+    ref["_q"], ref["_k"] = bits(wl.q), bits(wl.k)
+    gs, os_ = _check_tokens(ref, bits(out).reshape(B * T, cfg.hc_mult, cfg.dim)[pos],
+                            gate.cpu().numpy().reshape(B * T, -1)[pos], xb[pos], cfg)
+    say("   gate", gs, "out", os_)
+
+
+# ------------------------------------------------------------------ decode after prefill
+def test_decode_full(ge, dev):
+    say("decode: building tables")
+    wl = Workload(ge, "decode", dev)
+    cfg = wl.cfg
+    B, P, S = cfg.B, cfg.prefill, cfg.steps
+    pre = synth.token_ids(cfg, B, P, name="prefill_ids")
+    steps = synth.token_ids(cfg, B, S, name="step_ids")
+    state = torch.full((B, cfg.max_ngram_size - 1), cfg.pad_id, dtype=torch.int32, device=dev)
+    ost = oracle.HashState(B, P + S + 4)
+    ref_pre = oracle.hash_ids(wl.t, wl.geom, ost, pre)
+    got_pre = ge.engram_hash(wl.g, wl.tables, torch.from_numpy(pre).to(dev), state=state)
+    assert np.array_equal(got_pre.cpu().numpy(), ref_pre)
+    layer = ge.EngramLayer(wl.g, wl.tables, wl.table, wl.scales, wl.w, wl.q, wl.k)
+    check_steps = {0, 1, 2, 63, S - 1}
+    rows_to_check = np.array([0, 17, 40, B - 1])
+    for step in range(S):
+        ids_s = steps[:, step:step + 1].copy()
+        ids_t = torch.from_numpy(ids_s).to(dev)
+        ref_h = oracle.hash_ids(wl.t, wl.geom, ost, ids_s)
+        probe = state.clone()
+        got_h = ge.engram_hash(wl.g, wl.tables, ids_t, state=probe)
+        x = synth.activations(cfg, B, dev, name="x_step%d" % step).reshape(B, 1, cfg.hc_mult, cfg.dim)
+        gate = torch.empty((B, 1, cfg.hc_mult), dtype=torch.float32, device=dev)
+        out = layer.forward(x, ids_t, state=state, gate=gate)
+        assert np.array_equal(got_h.cpu().numpy(), ref_h), step
+        assert torch.equal(state, probe), step
+        if step in check_steps:
+            say("decode step", step)
+            h = ref_h[rows_to_check, 0]
+            tab, sc, inv = wl.host_rows(h)
+            rows = oracle.embed_rows(tab, sc, inv.reshape(-1)).reshape(len(rows_to_check), -1)
+            kv = oracle.linear(rows, bits(wl.w))
+            xb = bits(x).reshape(B, cfg.hc_mult, cfg.dim)[rows_to_check]
+            r_out, r_gate, r_a = oracle.gate_and_add(xb, kv, bits(wl.q), bits(wl.k), cfg.norm_eps)
+            ref = dict(kv=kv, out=r_out, gate=r_gate, a=r_a, _q=bits(wl.q), _k=bits(wl.k))
+            _check_tokens(ref, bits(out).reshape(B, cfg.hc_mult, cfg.dim)[rows_to_check],
+                          gate.cpu().numpy().reshape(B, -1)[rows_to_check], xb, cfg)
+    # after 512 + 128 tokens the state holds the last two compressed ids
+    assert np.array_equal(state.cpu().numpy(), wl.t["token_map"][steps[:, -2:]])
+
+
+# ------------------------------------------------------------------ gate stress
+def test_gate_stress_full(ge, dev):
+    cfg = synth.config("gate_stress")
+    t = synth.hash_tables(cfg)
+    from tests.gpu_util import geometry
+    g = geometry(ge, cfg, t["num_embeddings"])
+    n = cfg.n_tokens
+    say("gate stress: generating", n, "tokens")
+    x = synth.activations(cfg, n, dev)
+    q, k = synth.qk_weights(cfg, dev)
+    kv, cat = synth.gate_stress_kv(cfg, x, q, k)
+    gate = torch.empty((n, cfg.hc_mult), dtype=torch.float32, device=dev)
+    out = ge.engram_gate_add(g, x, kv, q, k, gate=gate)
+    torch.cuda.synchronize()
+    # every exactly-orthogonal key gives sigmoid(+sqrt(fp32(1e-6))) (within 1 ulp)
+    g0 = float(np.float32(1.0 / (1.0 + np.exp(-np.sqrt(np.float64(np.float32(1e-6)))))))
+    orth = cat == 0
+    say("gate stress: orthogonal pairs", int(orth.sum()))
+    gv = gate[orth]
+    assert torch.all(torch.abs(gv - g0) <= float(np.spacing(np.float32(g0)))).item()
+    pos = _sample_positions(n, n=48, seed=4)
+    xb = bits(x[torch.from_numpy(pos).to(dev)])
+    kvb = bits(kv[torch.from_numpy(pos).to(dev)])
+    r_out, r_gate, r_a = oracle.gate_and_add(xb, kvb, bits(q), bits(k), cfg.norm_eps)
+    gs = tolerances.check_gate(gate.cpu().numpy()[pos], r_gate, r_a)
+    os_ = tolerances.check_out(bits(out[torch.from_numpy(pos).to(dev)]), r_out, xb,
+                               kvb[:, cfg.hc_mult * cfg.dim:], gate.cpu().numpy()[pos], r_gate)
+    say("   gate", gs, "out", os_)
+    # the same launch twice gives the same bits
+    out2 = ge.engram_gate_add(g, x, kv, q, k)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+# ------------------------------------------------------------------ long mixed prefill
+def test_long_mixed_full(ge, dev):
+    say("long mixed: building tables")
+    wl = Workload(ge, "long_mixed", dev)
+    cfg = wl.cfg
+    B, T = cfg.B, cfg.T
+    ids_np = synth.token_ids(cfg, B, T)
+    mask_np = synth.token_mask(cfg, B, T)
+    assert 0.3 <= 1 - mask_np.mean() < 0.35
+    ids = torch.from_numpy(ids_np).to(dev)
+    mask = torch.from_numpy(mask_np).to(dev)
+    x = synth.activations(cfg, B * T, dev).reshape(B, T, cfg.hc_mult, cfg.dim)
+    gate = torch.empty((B, T, cfg.hc_mult), dtype=torch.float32, device=dev)
+    layer = ge.EngramLayer(wl.g, wl.tables, wl.table, wl.scales, wl.w, wl.q, wl.k)
+    out = layer.forward(x, ids, mask=mask, gate=gate)
+    torch.cuda.synchronize()
+    say("long mixed: masked positions pass through")
+    m = ~mask.reshape(-1)
+    assert torch.equal(out.reshape(B * T, -1)[m].view(torch.int16),
+                       x.reshape(B * T, -1)[m].view(torch.int16))
+    assert torch.all(gate.reshape(B * T, -1)[m] == 0).item()
+    say("long mixed: hash and gather for every position")
+    ref_hid = oracle.hash_ids(wl.t, wl.geom, oracle.HashState(B, T + 4), ids_np)
+    hid = ge.engram_hash(wl.g, wl.tables, ids)
+    assert np.array_equal(hid.cpu().numpy(), ref_hid)
+    tab, sc, inv = wl.host_rows(ref_hid)
+    ref_rows = oracle.embed_rows(tab, sc, inv.reshape(-1)).reshape(B * T, -1)
+    rows = ge.engram_gather(wl.g, wl.table, wl.scales, torch.from_numpy(ref_hid).to(dev))
+    assert np.array_equal(bits(rows).reshape(ref_rows.shape), ref_rows)
+    say("long mixed: end to end on sampled positions (span edges included)")
+    edges = np.nonzero(np.diff(mask_np[0].astype(np.int8)))[0]
+    pos = _sample_positions(T, extra=list(edges[:6]) + list(edges[:6] + 1), n=12, seed=5)
+    xb = bits(x).reshape(B * T, cfg.hc_mult, cfg.dim)[pos]
+    ref = _oracle_tokens(wl, ids_np[0], pos, xb, mask_np[0][pos])
+    ref["_q"], ref["_k"] = bits(wl.q), bits(wl.k)
+    gs, os_ = _check_tokens(ref, bits(out).reshape(B * T, cfg.hc_mult, cfg.dim)[pos],
+                            gate.cpu().numpy().reshape(B * T, -1)[pos], xb, cfg)
+    say("   gate", gs, "out", os_)
+
+
+def test_empty_calls_launch_nothing(ge, dev):
+    wl = Workload(ge, "tiny", dev)
+    cfg = wl.cfg
+    ids = torch.zeros((2, 0), dtype=torch.int32, device=dev)
+    x = torch.zeros((2, 0, cfg.hc_mult, cfg.dim), dtype=torch.bfloat16, device=dev)
+    out = ge.engram_forward(wl.g, wl.tables, wl.table, wl.scales, wl.w, wl.q, wl.k, x, ids)
+    assert out.shape == x.shape
+    assert ge.engram_hash(wl.g, wl.tables, ids).shape == (2, 0, synth.n_hash_cols(cfg))
+    a = torch.zeros((0, wl.g.K), dtype=torch.bfloat16, device=dev)
+    assert ge.engram_wkv(wl.g, a, wl.w).shape == (0, wl.g.N)

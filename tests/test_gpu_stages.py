@@ -247,6 +247,25 @@ def test_gate_full_width_stress_recipe(ge, dev):
     assert np.all(np.abs(gv - g0) <= np.spacing(g0)), gv[:4]
 
 
+@pytest.mark.parametrize("hc,dim,n_tok", [(3, 16384, 6), (8, 32768, 3), (1, 8, 50), (2, 1000, 33)])
+def test_gate_other_geometries(ge, dev, hc, dim, n_tok):
+    # streaming variant (x and value re-read), tiny dims, odd chunk counts
+    g = ge.Geometry.make(dim=dim, hc_mult=hc, max_ngram_size=2, n_heads=1, head_dim=32,
+                         num_embeddings=1, vocab=1)
+    say("gate hc", hc, "dim", dim)
+    gen = torch.Generator(device=dev).manual_seed(hc * 7 + dim)
+    x = torch.randn((n_tok, hc, dim), generator=gen, device=dev).to(torch.bfloat16)
+    key = x.float() * torch.rand((n_tok, hc, 1), generator=gen, device=dev) * 2 - x.float() * 0.5
+    key = key + 0.3 * torch.randn((n_tok, hc, dim), generator=gen, device=dev)
+    v = torch.randn((n_tok, dim), generator=gen, device=dev)
+    kv = torch.cat([key.reshape(n_tok, hc * dim), v], dim=1).to(torch.bfloat16)
+    q = (1 + 0.1 * torch.rand((hc, dim), generator=gen, device=dev)).to(torch.bfloat16)
+    k = (1 + 0.1 * torch.rand((hc, dim), generator=gen, device=dev)).to(torch.bfloat16)
+    mask = torch.ones(n_tok, dtype=torch.bool, device=dev)
+    mask[n_tok // 2] = False
+    _gate_check(ge, g, x, kv, q, k, mask=mask)
+
+
 def test_gate_mask_and_in_place(ge, dev, tiny):
     say("gate mask in place")
     x, kv, q, k, _ = _gate_inputs(tiny.cfg, 40, dev, name="m")

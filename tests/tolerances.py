@@ -84,10 +84,14 @@ def key_ulp_da(x_bits, key_bits, q_bits, k_bits, eps):
     return 2.0 * (d_hwk * rstd / math.sqrt(D) + np.abs(a) * 0.5 * (d_kk / D) / (skk / D + eps))
 
 
-def check_gate(g, g_ref, a_ref, rtol=1e-5, da=None, min_tight=0.9):
+def check_gate(g, g_ref, a_ref, rtol=1e-5, da=None, min_tight=0.5):
     """da: optional bound on |a - a_ref| from inputs that differ (end to end);
     it widens the bound by its first-order effect on g and the band by da,
-    and then at least `min_tight` of the live gates must still meet rtol."""
+    and then at least `min_tight` of the live gates must still meet rtol.
+    (End to end, a key of dim elements is bit-identical to the oracle's with
+    probability about p^dim, p = the kv bit-equal fraction: ~0.97 at dim 256,
+    ~0.6 at dim 5120 for p = 0.9999; the gates of the other keys are held to
+    the propagated bound.)"""
     g = np.asarray(g, np.float64)
     g_ref = np.asarray(g_ref, np.float64)
     a_ref = np.asarray(a_ref, np.float64)
