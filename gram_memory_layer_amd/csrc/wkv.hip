@@ -177,6 +177,19 @@ wkv_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, int64
     }
 }
 
+template <int BM, int BN, int WM, int WN>
+hipError_t run(const uint16_t* a, const uint16_t* w, int64_t M, int N, int K, uint16_t* kv,
+               hipStream_t s) {
+    constexpr int NT = (BM / WM) * (BN / WN) * 64;
+    const int tiles_m = (int)((M + BM - 1) / BM);
+    const int tiles_n = (N + BN - 1) / BN;
+    const int total = tiles_m * tiles_n;
+    const int per_xcd = (total + N_XCD - 1) / N_XCD;
+    wkv_kernel<BM, BN, WM, WN>
+        <<<dim3(per_xcd * N_XCD), dim3(NT), 0, s>>>(a, w, M, N, K, kv, tiles_m, tiles_n, per_xcd);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // Main kernel for K % 64 == 0: 256 x 256 output tiles, 4 waves of 128 x 128,
 // k-tiles of 64 double-buffered in LDS (2 x 64 KiB).
@@ -191,8 +204,7 @@ wkv_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, int64
 // ring of 32-wide k-tiles, measured slower on this shape.)  Within a k-tile the
 // fragments of the next 16-wide k-step are read from LDS while the current
 // k-step's 16 MFMAs issue.
-constexpr int F_BM = 256, F_BN = 256, F_WM = 128, F_WN = 128, F_NT = 256;
-constexpr int F_STAGE = (F_BM + F_BN) * 128;  // bytes per LDS stage
+constexpr int F_NT = 256;  // 4 waves in a 2 x 2 arrangement
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -211,10 +223,18 @@ __device__ __forceinline__ int slot128(int row, int c) {
     return c ^ ((row & 7) ^ ((row >> 3) & 1));
 }
 
-__global__ void __launch_bounds__(F_NT, 1)
-wkv_fast_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, int64_t M, int N,
-                int K, uint16_t* __restrict__ C, int tiles_m, int tiles_n, int per_xcd) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * F_STAGE];
+// BT x BT output tiles (BT = 256: 128 x 128 per wave; BT = 128: 64 x 64 per
+// wave).  Columns [0, N) of this launch start at W row 0 and C column 0; C
+// rows are `ldc` elements apart.
+template <int BT>
+__device__ __forceinline__ void wkv_tile(const uint16_t* __restrict__ A,
+                                         const uint16_t* __restrict__ W, int64_t M, int N, int K,
+                                         uint16_t* __restrict__ C, int64_t ldc, int tiles_m,
+                                         int tiles_n, int per_xcd, uint8_t* smem) {
+    constexpr int BM = BT, BN = BT, WM = BT / 2, WN = BT / 2;
+    constexpr int TI = WM / 32, TJ = WN / 32;  // 32 x 32 MFMA tiles per wave
+    constexpr int NLD = BT / 32;               // LDS-bound loads per wave per operand
+    constexpr int STAGE = (BM + BN) * 128;     // bytes per LDS stage
 
     const int b = blockIdx.x;
     const int L = (b % N_XCD) * per_xcd + b / N_XCD;
@@ -224,82 +244,83 @@ wkv_fast_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, 
     const int gm = min(tiles_m - first_m, GROUP_M);
     const int mt = first_m + (L % group_size) % gm;
     const int nt = (L % group_size) / gm;
-    const int64_t m0 = (int64_t)mt * F_BM;
-    const int n0 = nt * F_BN;
+    const int64_t m0 = (int64_t)mt * BM;
+    const int n0 = nt * BN;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
 
-    const int64_t rows_a = min((int64_t)F_BM, M - m0);
-    const int rows_w = min(F_BN, N - n0);
+    const int64_t rows_a = min((int64_t)BM, M - m0);
+    const int rows_w = min(BN, N - n0);
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + m0 * K, (uint32_t)(rows_a * K * 2));
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (int64_t)n0 * K, (uint32_t)(rows_w * K * 2));
 
-    // load slots: instruction i (0..7) of this wave fills LDS segment
+    // load slots: instruction i of this wave fills LDS segment
     // seg = 4*i + wave = rows 8*seg .. 8*seg+7 of the A rows (then the W rows)
-    uint32_t voff[8];
+    uint32_t voff[NLD];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < NLD; ++i) {
         const int row = (4 * i + wave) * 8 + (lane >> 3);
         voff[i] = (uint32_t)(row * K * 2 + slot128(row, lane & 7) * 16);
     }
     auto issue_loads = [&](int kt, int stage) {
-        uint8_t* st = smem + stage * F_STAGE;
+        uint8_t* st = smem + stage * STAGE;
         const int soff = kt * 128;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < NLD; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 ra, (lds_void*)(st + (4 * i + wave) * 1024), 16, voff[i], soff, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < NLD; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rw, (lds_void*)(st + F_BM * 128 + (4 * i + wave) * 1024), 16, voff[i], soff, 0, 0);
+                rw, (lds_void*)(st + BM * 128 + (4 * i + wave) * 1024), 16, voff[i], soff, 0, 0);
     };
 
     const int lrow = lane & 31, lhalf = lane >> 5;
-    bf16x8 fa[2][4], fw[2][4];
+    bf16x8 fa[2][TI], fw[2][TJ];
     auto read_frags = [&](int stage, int ks, int buf) {
-        const uint8_t* st = smem + stage * F_STAGE;
+        const uint8_t* st = smem + stage * STAGE;
         const int c = ks * 2 + lhalf;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = wm * F_WM + i * 32 + lrow;
+        for (int i = 0; i < TI; ++i) {
+            const int row = wm * WM + i * 32 + lrow;
             fa[buf][i] = *reinterpret_cast<const bf16x8*>(st + row * 128 + slot128(row, c) * 16);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = wn * F_WN + j * 32 + lrow;
-            fw[buf][j] = *reinterpret_cast<const bf16x8*>(st + F_BM * 128 + row * 128 +
+        for (int j = 0; j < TJ; ++j) {
+            const int row = wn * WN + j * 32 + lrow;
+            fw[buf][j] = *reinterpret_cast<const bf16x8*>(st + BM * 128 + row * 128 +
                                                           slot128(row, c) * 16);
         }
     };
 
-    f32x16 acc[4][4];
+    f32x16 acc[TJ][TI];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < TI; ++i)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
 
-    auto mfma_half = [&](int cur, int j0) {
+    auto mfma_half = [&](int cur, int half) {
 #pragma unroll
-        for (int j = j0; j < j0 + 2; ++j)
+        for (int j = half * (TJ / 2); j < (half + 1) * (TJ / 2); ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < TI; ++i)
                 acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[cur][j], fa[cur][i],
                                                                     acc[j][i], 0, 0, 0);
     };
-    // One k-tile = 4 k-steps of 16 MFMAs, each k-step its own scheduling
+    // One k-tile = 4 k-steps of TI*TJ MFMAs, each k-step its own scheduling
     // region (sched_barrier fences stop the compiler from regrouping MFMAs by
     // accumulator across k-steps, which would chain dependent MFMAs).  The
-    // next k-step's 8 fragment reads are interleaved with the current MFMAs;
-    // the next k-tile's 16 LDS-bound buffer loads go out during k-step 0.  The
-    // last k-step is split around the barrier so that the next k-tile's first
-    // fragment reads overlap its second half.
+    // next k-step's TI+TJ fragment reads are interleaved with the current
+    // MFMAs; the next k-tile's LDS-bound buffer loads go out during k-step 0.
+    // The last k-step is split around the barrier so that the next k-tile's
+    // first fragment reads overlap its second half.
     //   LOADS: k-tile kt+1 exists (its loads are issued here)
+    constexpr int NRD = TI + TJ, NMF = TI * TJ;
     auto k_tile = [&](int kt, auto with_loads) {
         constexpr bool LOADS = decltype(with_loads)::value;
         const int stage = kt & 1;
@@ -309,14 +330,14 @@ wkv_fast_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, 
             if (LOADS && ks == 0) issue_loads(kt + 1, stage ^ 1);
             read_frags(stage, ks + 1, cur ^ 1);
             mfma_half(cur, 0);
-            mfma_half(cur, 2);
+            mfma_half(cur, 1);
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                if (LOADS && ks == 0) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+            for (int r = 0; r < NRD; ++r) {
+                if (LOADS && ks == 0) __builtin_amdgcn_sched_group_barrier(0x020, 2 * NLD / NRD, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+            if (NMF > NRD) __builtin_amdgcn_sched_group_barrier(0x008, NMF - NRD, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
         mfma_half(1, 0);
@@ -327,12 +348,12 @@ wkv_fast_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, 
             __builtin_amdgcn_sched_barrier(0);
             read_frags(stage ^ 1, 0, 0);
         }
-        mfma_half(1, 2);
+        mfma_half(1, 1);
         if constexpr (LOADS) {
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
+            for (int r = 0; r < NRD; ++r) {
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (r < NMF / 2) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -350,60 +371,106 @@ wkv_fast_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, 
     __syncthreads();  // every wave is done with the operand stages
 
     // ---- epilogue through LDS.  D[n][m]: lane holds m = lane%32 (+32 i) and
-    // n = 32 j + 8 (v/4) + 4 (lane/32) + v%4.  Each wave writes its 128 x 128
-    // block as bf16 rows [m][n] into its own 32 KiB of LDS (16-byte chunks
-    // XOR-swizzled by row), then reads it back so that 16 lanes store one
-    // 256-byte row run with 16-byte stores.
-    uint8_t* ep = smem + wave * (128 * 256);
+    // n = 32 j + 8 (v/4) + 4 (lane/32) + v%4.  Each wave writes its WM x WN
+    // block as bf16 rows [m][n] into its own part of LDS (16-byte chunks
+    // XOR-swizzled by row), then reads it back so that consecutive lanes store
+    // one WN*2-byte row run with 16-byte stores.
+    constexpr int RB = WN * 2;            // bytes per epilogue row
+    constexpr int CHW = RB / 16;          // 16-byte chunks per row
+    constexpr int RPI = 64 / CHW;         // rows per store instruction
+    uint8_t* ep = smem + wave * (WM * RB);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < TI; ++i)
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
                 const int r = i * 32 + lrow;
                 const int nn = j * 32 + 8 * g4 + 4 * lhalf;  // multiple of 4
-                const int ch = (nn >> 3) ^ (r & 15);
+                const int ch = (nn >> 3) ^ (r & (CHW - 1));
                 const uint32_t lo = f32_to_bf16(acc[j][i][4 * g4 + 0]) |
                                     (f32_to_bf16(acc[j][i][4 * g4 + 1]) << 16);
                 const uint32_t hi = f32_to_bf16(acc[j][i][4 * g4 + 2]) |
                                     (f32_to_bf16(acc[j][i][4 * g4 + 3]) << 16);
-                *reinterpret_cast<uint2*>(ep + r * 256 + ch * 16 + (nn & 4) * 2) =
+                *reinterpret_cast<uint2*>(ep + r * RB + ch * 16 + (nn & 4) * 2) =
                     make_uint2(lo, hi);
             }
-    const int rsub = lane >> 4, csub = lane & 15;
+    const int rsub = lane / CHW, csub = lane % CHW;
 #pragma unroll 4
-    for (int it = 0; it < 32; ++it) {
-        const int r = it * 4 + rsub;
-        const uint4 v = *reinterpret_cast<const uint4*>(ep + r * 256 + ((csub ^ (r & 15)) << 4));
-        const int64_t m = m0 + wm * F_WM + r;
-        const int n = n0 + wn * F_WN + csub * 8;
-        if (m < M && n < N) *reinterpret_cast<uint4*>(C + m * N + n) = v;
+    for (int it = 0; it < WM / RPI; ++it) {
+        const int r = it * RPI + rsub;
+        const uint4 v =
+            *reinterpret_cast<const uint4*>(ep + r * RB + ((csub ^ (r & (CHW - 1))) << 4));
+        const int64_t m = m0 + wm * WM + r;
+        const int n = n0 + wn * WN + csub * 8;
+        if (m < M && n < N) *reinterpret_cast<uint4*>(C + m * ldc + n) = v;
     }
 }
 
-hipError_t run_fast(const uint16_t* a, const uint16_t* w, int64_t M, int N, int K, uint16_t* kv,
-                    hipStream_t s) {
-    const int tiles_m = (int)((M + F_BM - 1) / F_BM);
-    const int tiles_n = (N + F_BN - 1) / F_BN;
+__global__ void __launch_bounds__(F_NT, 1)
+wkv_fast_256(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, int64_t M, int N,
+             int K, uint16_t* __restrict__ C, int64_t ldc, int tiles_m, int tiles_n, int per_xcd) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * (256 + 256) * 128];
+    wkv_tile<256>(A, W, M, N, K, C, ldc, tiles_m, tiles_n, per_xcd, smem);
+}
+
+__global__ void __launch_bounds__(F_NT, 1)
+wkv_fast_128(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, int64_t M, int N,
+             int K, uint16_t* __restrict__ C, int64_t ldc, int tiles_m, int tiles_n, int per_xcd) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * (128 + 128) * 128];
+    wkv_tile<128>(A, W, M, N, K, C, ldc, tiles_m, tiles_n, per_xcd, smem);
+}
+
+template <int BT>
+hipError_t run_fast(const uint16_t* a, const uint16_t* w, int64_t M, int N, int K, uint16_t* c,
+                    int64_t ldc, hipStream_t s) {
+    const int tiles_m = (int)((M + BT - 1) / BT);
+    const int tiles_n = (N + BT - 1) / BT;
     const int total = tiles_m * tiles_n;
     const int per_xcd = (total + N_XCD - 1) / N_XCD;
-    wkv_fast_kernel<<<dim3(per_xcd * N_XCD), dim3(F_NT), 0, s>>>(a, w, M, N, K, kv, tiles_m,
-                                                                 tiles_n, per_xcd);
+    auto kern = BT == 256 ? wkv_fast_256 : wkv_fast_128;
+    kern<<<dim3(per_xcd * N_XCD), dim3(F_NT), 0, s>>>(a, w, M, N, K, c, ldc, tiles_m, tiles_n,
+                                                      per_xcd);
     return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN>
-hipError_t run(const uint16_t* a, const uint16_t* w, int64_t M, int N, int K, uint16_t* kv,
-               hipStream_t s) {
-    constexpr int NT = (BM / WM) * (BN / WN) * 64;
-    const int tiles_m = (int)((M + BM - 1) / BM);
-    const int tiles_n = (N + BN - 1) / BN;
-    const int total = tiles_m * tiles_n;
-    const int per_xcd = (total + N_XCD - 1) / N_XCD;
-    wkv_kernel<BM, BN, WM, WN>
-        <<<dim3(per_xcd * N_XCD), dim3(NT), 0, s>>>(a, w, M, N, K, kv, tiles_m, tiles_n, per_xcd);
-    return hipGetLastError();
+int cu_count() {
+    static int n = 0;
+    if (n == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            v > 0)
+            n = v;
+        else
+            n = 256;
+    }
+    return n;
+}
+
+// Main path: 256 x 256 tiles over the widest column range whose tile count
+// fills whole rounds of the machine, and the remaining columns in 128 x 128
+// tiles when those fit in one round (T=4096, N=25600: 1536 big tiles = 6
+// rounds, then 256 small tiles, instead of 7 rounds with the last one a
+// quarter full).
+hipError_t run_main(const uint16_t* a, const uint16_t* w, int64_t M, int N, int K, uint16_t* kv,
+                    hipStream_t s) {
+    const int cus = cu_count();
+    const int tiles_m = (int)((M + 255) / 256);
+    const int tiles_n = (N + 255) / 256;
+    int nb = tiles_n;
+    if ((int64_t)tiles_m * tiles_n % cus != 0) {
+        int cand = tiles_n - 1;
+        while (cand > 0 && (int64_t)tiles_m * cand % cus != 0) --cand;
+        if (cand > 0) {
+            const int64_t small = ((M + 127) / 128) * ((N - cand * 256 + 127) / 128);
+            if (small <= cus) nb = cand;
+        }
+    }
+    hipError_t e = run_fast<256>(a, w, M, nb * 256 < N ? nb * 256 : N, K, kv, N, s);
+    if (e != hipSuccess || nb * 256 >= N) return e;
+    return run_fast<128>(a, w + (int64_t)nb * 256 * K, M, N - nb * 256, K, kv + (int64_t)nb * 256, N,
+                         s);
 }
 
 }  // namespace
@@ -411,8 +478,8 @@ hipError_t run(const uint16_t* a, const uint16_t* w, int64_t M, int N, int K, ui
 hipError_t launch_wkv(const uint16_t* a, const uint16_t* w, int64_t M, int N, int K,
                       uint16_t* kv, hipStream_t s) {
     if (M == 0) return hipSuccess;
-    if (M >= 1024 && K % BK == 0 && (int64_t)K * 2 * F_BM < (1ll << 31))
-        return run_fast(a, w, M, N, K, kv, s);
+    if (M >= 1024 && K % BK == 0 && (int64_t)K * 2 * 256 < (1ll << 31))
+        return run_main(a, w, M, N, K, kv, s);
     if (M >= 1024) return run<256, 256, 128, 128>(a, w, M, N, K, kv, s);
     return run<64, 64, 32, 32>(a, w, M, N, K, kv, s);
 }

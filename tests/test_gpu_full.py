@@ -113,6 +113,28 @@ def test_prefill_full(ge, dev):
     say("   gate", gs, "out", os_)
 
 
+# ------------------------------------------------------------------ projection tiling
+@pytest.mark.parametrize("M", [2048, 4096])
+def test_wkv_full_width_tail_split(ge, dev, M):
+    # full N = 25600 with K = 1536: 256 x 256 tiles over the first 24576
+    # columns (whole rounds of the machine), 128 x 128 tiles over the rest
+    cfg = synth.config("prefill")
+    from tests.gpu_util import geometry
+    g = geometry(ge, cfg, 1)
+    say("wkv full width M", M)
+    gen = torch.Generator(device=dev).manual_seed(M)
+    a = torch.randn((M, g.K), generator=gen, device=dev).to(torch.bfloat16)
+    w = synth.wkv_weight(cfg, dev)
+    kv = ge.engram_wkv(g, a, w)
+    rows = np.unique(np.concatenate([[0, 127, 128, 255, 256, M - 129, M - 128, M - 1],
+                                     np.random.default_rng(M).integers(0, M, 8)]))
+    ab = bits(a[torch.from_numpy(rows).to(dev)])
+    ref = oracle.linear(ab, bits(w))
+    absdot = np.abs(tolerances.bf16_value(ab)) @ np.abs(tolerances.bf16_value(bits(w))).T
+    st = tolerances.check_kv(bits(kv[torch.from_numpy(rows).to(dev)]), ref, absdot, g.K)
+    say("   kv", st)
+
+
 # ------------------------------------------------------------------ decode after prefill
 def test_decode_full(ge, dev):
     say("decode: building tables")
