@@ -204,7 +204,8 @@ hipError_t run(const uint16_t* a, const uint16_t* w, int64_t M, int N, int K, ui
 // ring of 32-wide k-tiles, measured slower on this shape.)  Within a k-tile the
 // fragments of the next 16-wide k-step are read from LDS while the current
 // k-step's 16 MFMAs issue.
-constexpr int F_NT = 256;  // 4 waves in a 2 x 2 arrangement
+constexpr int F_NT = 256;  // 4 waves in a 2 x 2 arrangement (the 8-wave variant: 512)
+constexpr bool WAVES8 = true;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -226,14 +227,15 @@ __device__ __forceinline__ int slot128(int row, int c) {
 // BT x BT output tiles (BT = 256: 128 x 128 per wave; BT = 128: 64 x 64 per
 // wave).  Columns [0, N) of this launch start at W row 0 and C column 0; C
 // rows are `ldc` elements apart.
-template <int BT>
+template <int BT, int WMV = 2, int WNV = 2>
 __device__ __forceinline__ void wkv_tile(const uint16_t* __restrict__ A,
                                          const uint16_t* __restrict__ W, int64_t M, int N, int K,
                                          uint16_t* __restrict__ C, int64_t ldc, int tiles_m,
                                          int tiles_n, int per_xcd, uint8_t* smem) {
-    constexpr int BM = BT, BN = BT, WM = BT / 2, WN = BT / 2;
+    constexpr int NW = WMV * WNV;              // waves: WMV along m, WNV along n
+    constexpr int BM = BT, BN = BT, WM = BT / WMV, WN = BT / WNV;
     constexpr int TI = WM / 32, TJ = WN / 32;  // 32 x 32 MFMA tiles per wave
-    constexpr int NLD = BT / 32;               // LDS-bound loads per wave per operand
+    constexpr int NLD = BT / 8 / NW;           // LDS-bound loads per wave per operand
     constexpr int STAGE = (BM + BN) * 128;     // bytes per LDS stage
 
     const int b = blockIdx.x;
@@ -250,7 +252,7 @@ __device__ __forceinline__ void wkv_tile(const uint16_t* __restrict__ A,
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WNV, wn = wave % WNV;
 
     const int64_t rows_a = min((int64_t)BM, M - m0);
     const int rows_w = min(BN, N - n0);
@@ -258,11 +260,11 @@ __device__ __forceinline__ void wkv_tile(const uint16_t* __restrict__ A,
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (int64_t)n0 * K, (uint32_t)(rows_w * K * 2));
 
     // load slots: instruction i of this wave fills LDS segment
-    // seg = 4*i + wave = rows 8*seg .. 8*seg+7 of the A rows (then the W rows)
+    // seg = NW*i + wave = rows 8*seg .. 8*seg+7 of the A rows (then the W rows)
     uint32_t voff[NLD];
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-        const int row = (4 * i + wave) * 8 + (lane >> 3);
+        const int row = (NW * i + wave) * 8 + (lane >> 3);
         voff[i] = (uint32_t)(row * K * 2 + slot128(row, lane & 7) * 16);
     }
     auto issue_loads = [&](int kt, int stage) {
@@ -271,11 +273,11 @@ __device__ __forceinline__ void wkv_tile(const uint16_t* __restrict__ A,
 #pragma unroll
         for (int i = 0; i < NLD; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                ra, (lds_void*)(st + (4 * i + wave) * 1024), 16, voff[i], soff, 0, 0);
+                ra, (lds_void*)(st + (NW * i + wave) * 1024), 16, voff[i], soff, 0, 0);
 #pragma unroll
         for (int i = 0; i < NLD; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rw, (lds_void*)(st + BM * 128 + (4 * i + wave) * 1024), 16, voff[i], soff, 0, 0);
+                rw, (lds_void*)(st + BM * 128 + (NW * i + wave) * 1024), 16, voff[i], soff, 0, 0);
     };
 
     const int lrow = lane & 31, lhalf = lane >> 5;
@@ -331,13 +333,32 @@ __device__ __forceinline__ void wkv_tile(const uint16_t* __restrict__ A,
             read_frags(stage, ks + 1, cur ^ 1);
             mfma_half(cur, 0);
             mfma_half(cur, 1);
+            if constexpr ((2 * NLD) % NRD == 0) {
 #pragma unroll
-            for (int r = 0; r < NRD; ++r) {
-                if (LOADS && ks == 0) __builtin_amdgcn_sched_group_barrier(0x020, 2 * NLD / NRD, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                for (int r = 0; r < NRD; ++r) {
+                    if (LOADS && ks == 0)
+                        __builtin_amdgcn_sched_group_barrier(0x020, 2 * NLD / NRD, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                if (NMF > NRD) __builtin_amdgcn_sched_group_barrier(0x008, NMF - NRD, 0);
+            } else if (LOADS && ks == 0) {
+                constexpr int RR = 2 * NLD > NRD ? 2 * NLD : NRD;
+#pragma unroll
+                for (int r = 0; r < RR; ++r) {
+                    if (r < 2 * NLD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                    if (r < NMF) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (r < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                if constexpr (NMF > RR) __builtin_amdgcn_sched_group_barrier(0x008, NMF - RR, 0);
+            } else {
+#pragma unroll
+                for (int r = 0; r < NRD; ++r) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                if constexpr (NMF > NRD) __builtin_amdgcn_sched_group_barrier(0x008, NMF - NRD, 0);
             }
-            if (NMF > NRD) __builtin_amdgcn_sched_group_barrier(0x008, NMF - NRD, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
         mfma_half(1, 0);
@@ -414,6 +435,14 @@ wkv_fast_256(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, int
     wkv_tile<256>(A, W, M, N, K, C, ldc, tiles_m, tiles_n, per_xcd, smem);
 }
 
+__global__ void __launch_bounds__(2 * F_NT, 1)
+wkv_fast_256w8(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, int64_t M, int N,
+               int K, uint16_t* __restrict__ C, int64_t ldc, int tiles_m, int tiles_n,
+               int per_xcd) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * (256 + 256) * 128];
+    wkv_tile<256, 2, 4>(A, W, M, N, K, C, ldc, tiles_m, tiles_n, per_xcd, smem);
+}
+
 __global__ void __launch_bounds__(F_NT, 1)
 wkv_fast_128(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, int64_t M, int N,
              int K, uint16_t* __restrict__ C, int64_t ldc, int tiles_m, int tiles_n, int per_xcd) {
@@ -428,9 +457,14 @@ hipError_t run_fast(const uint16_t* a, const uint16_t* w, int64_t M, int N, int 
     const int tiles_n = (N + BT - 1) / BT;
     const int total = tiles_m * tiles_n;
     const int per_xcd = (total + N_XCD - 1) / N_XCD;
-    auto kern = BT == 256 ? wkv_fast_256 : wkv_fast_128;
-    kern<<<dim3(per_xcd * N_XCD), dim3(F_NT), 0, s>>>(a, w, M, N, K, c, ldc, tiles_m, tiles_n,
-                                                      per_xcd);
+    if (BT == 256 && WAVES8) {
+        wkv_fast_256w8<<<dim3(per_xcd * N_XCD), dim3(2 * F_NT), 0, s>>>(a, w, M, N, K, c, ldc,
+                                                                       tiles_m, tiles_n, per_xcd);
+    } else {
+        auto kern = BT == 256 ? wkv_fast_256 : wkv_fast_128;
+        kern<<<dim3(per_xcd * N_XCD), dim3(F_NT), 0, s>>>(a, w, M, N, K, c, ldc, tiles_m, tiles_n,
+                                                          per_xcd);
+    }
     return hipGetLastError();
 }
 
