@@ -8,8 +8,9 @@ pointers through the C ABI declared in ``include/engram.h`` and raise
 library is not built, every call raises.
 
 Functions carry the C names:
-    engram_hash, engram_gather, engram_wkv, engram_gate_add, engram_forward,
-    engram_forward_workspace_size, engram_check_geometry
+    engram_hash, engram_gather, engram_wkv, engram_wkv_gathered, engram_gate_add,
+    engram_forward, engram_forward_workspace_size, engram_wkv_gathered_scratch_size,
+    engram_check_geometry
 plus ``Geometry`` / ``HashTables`` (the C structs) and ``EngramLayer``, a
 holder for one layer's device tables, weights and workspace.
 """
@@ -23,6 +24,7 @@ import torch
 __all__ = [
     "Geometry", "HashTables", "EngramError", "EngramLayer", "load", "library_path",
     "engram_check_geometry", "engram_hash", "engram_gather", "engram_wkv",
+    "engram_wkv_gathered", "engram_wkv_gathered_scratch_size",
     "engram_gate_add", "engram_forward", "engram_forward_workspace_size",
     "ERRBIT_TOKEN", "ERRBIT_HASH", "ERRBIT_ROW",
 ]
@@ -98,6 +100,10 @@ def load():
     L.engram_gather.argtypes = [G, P, P, P, i64, P, P, P]
     L.engram_wkv.restype = C.c_int
     L.engram_wkv.argtypes = [G, P, P, i64, P, P]
+    L.engram_wkv_gathered_scratch_size.restype = C.c_size_t
+    L.engram_wkv_gathered_scratch_size.argtypes = [G, i64]
+    L.engram_wkv_gathered.restype = C.c_int
+    L.engram_wkv_gathered.argtypes = [G, P, P, P, i64, P, P, P, C.c_size_t, P, P]
     L.engram_gate_add.restype = C.c_int
     L.engram_gate_add.argtypes = [G, P, P, P, P, P, i64, P, P, P]
     L.engram_forward_workspace_size.restype = C.c_size_t
@@ -214,6 +220,36 @@ def engram_wkv(g: Geometry, a, w, kv=None):
     _dev(kv, "kv", torch.bfloat16, (M, g.N), dev)
     _check("engram_wkv", L.engram_wkv(C.byref(g), a.data_ptr(), w.data_ptr(), M, kv.data_ptr(),
                                       _stream(dev)))
+    return kv
+
+
+def engram_wkv_gathered_scratch_size(g: Geometry, M: int) -> int:
+    return load().engram_wkv_gathered_scratch_size(C.byref(g), int(M))
+
+
+def engram_wkv_gathered(g: Geometry, table, scales, hash_ids, w, kv=None, scratch=None, err=None):
+    """Gather + projection in one: table/scales/hash_ids as in engram_gather,
+    w bf16 [N, K] -> kv bf16 [n_tok, N] (head_dim 64 only)."""
+    L = load()
+    dev = hash_ids.device
+    _dev(table, "table", torch.uint8, (g.num_embeddings, g.head_dim), dev)
+    _dev(scales, "scales", torch.uint8, (g.num_embeddings, g.head_dim // 32), dev)
+    _dev(hash_ids, "hash_ids", torch.int32, None, dev)
+    hid = hash_ids.reshape(-1, g.n_hash_cols)
+    M = hid.shape[0]
+    _dev(w, "w", torch.bfloat16, (g.N, g.K), dev)
+    if kv is None:
+        kv = torch.empty((M, g.N), dtype=torch.bfloat16, device=dev)
+    _dev(kv, "kv", torch.bfloat16, (M, g.N), dev)
+    need = engram_wkv_gathered_scratch_size(g, M)
+    if scratch is None:
+        scratch = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev(scratch, "scratch", torch.uint8, None, dev)
+    if err is not None:
+        _dev(err, "err", torch.int32, (1,), dev)
+    _check("engram_wkv_gathered", L.engram_wkv_gathered(
+        C.byref(g), table.data_ptr(), scales.data_ptr(), hid.data_ptr(), M, w.data_ptr(),
+        kv.data_ptr(), scratch.data_ptr(), scratch.numel(), _ptr(err), _stream(dev)))
     return kv
 
 

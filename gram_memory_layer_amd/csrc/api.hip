@@ -110,6 +110,31 @@ engram_status engram_wkv(const engram_geometry* g, const uint16_t* a, const uint
     return from_hip(engram::launch_wkv(a, w, M, gg.N, gg.K, kv, (hipStream_t)stream));
 }
 
+size_t engram_wkv_gathered_scratch_size(const engram_geometry* g, int64_t M) {
+    if (engram_check_geometry(g) != ENGRAM_OK || M < 0) return 0;
+    return engram::gathered_scratch_bytes(engram::make_geom(*g), M);
+}
+
+engram_status engram_wkv_gathered(const engram_geometry* g, const uint8_t* table,
+                                  const uint8_t* scales, const int32_t* hash_ids, int64_t M,
+                                  const uint16_t* w, uint16_t* kv, void* scratch,
+                                  size_t scratch_bytes, uint32_t* err, void* stream) {
+    engram_status st = engram_check_geometry(g);
+    if (st != ENGRAM_OK) return st;
+    if (M < 0 || M >= kMaxTokens) return ENGRAM_ERR_INVALID_ARG;
+    const Geom gg = engram::make_geom(*g);
+    if (!engram::gathered_supported(gg, M)) return ENGRAM_ERR_UNSUPPORTED;
+    if (M == 0) return ENGRAM_OK;
+    if (!table || !scales || !hash_ids || !w || !kv) return ENGRAM_ERR_INVALID_ARG;
+    if (!aligned16(table) || !aligned16(w) || !aligned16(kv) || ((uintptr_t)hash_ids & 3u) != 0)
+        return ENGRAM_ERR_INVALID_ARG;
+    if (scratch == nullptr || scratch_bytes < engram::gathered_scratch_bytes(gg, M) ||
+        ((uintptr_t)scratch & 255u) != 0)
+        return ENGRAM_ERR_WORKSPACE;
+    return from_hip(engram::launch_wkv_gathered(gg, hash_ids, table, scales, w, M, kv, scratch,
+                                                err, (hipStream_t)stream));
+}
+
 engram_status engram_gate_add(const engram_geometry* g, const uint16_t* x, const uint16_t* kv,
                               const uint16_t* q, const uint16_t* k, const uint8_t* mask,
                               int64_t n_tok, uint16_t* out, float* gate, void* stream) {
@@ -128,9 +153,10 @@ engram_status engram_gate_add(const engram_geometry* g, const uint16_t* x, const
 size_t engram_forward_workspace_size(const engram_geometry* g, int64_t n_tok) {
     if (engram_check_geometry(g) != ENGRAM_OK || n_tok < 0) return 0;
     const Geom gg = engram::make_geom(*g);
+    const size_t rows = (size_t)n_tok * gg.K * sizeof(uint16_t);
+    const size_t scl = engram::gathered_scratch_bytes(gg, n_tok);
     return align256((size_t)n_tok * gg.n_cols * sizeof(int32_t)) +
-           align256((size_t)n_tok * gg.K * sizeof(uint16_t)) +
-           align256((size_t)n_tok * gg.N * sizeof(uint16_t));
+           align256(rows > scl ? rows : scl) + align256((size_t)n_tok * gg.N * sizeof(uint16_t));
 }
 
 engram_status engram_forward(const engram_geometry* g, const engram_hash_tables* t,
@@ -157,13 +183,26 @@ engram_status engram_forward(const engram_geometry* g, const engram_hash_tables*
     char* ws = (char*)workspace;
     int32_t* hash_ids = (int32_t*)ws;
     ws += align256((size_t)n_tok * gg.n_cols * sizeof(int32_t));
-    uint16_t* rows = (uint16_t*)ws;
-    ws += align256((size_t)n_tok * gg.K * sizeof(uint16_t));
+    uint16_t* rows = (uint16_t*)ws;  // or the fused projection's scratch
+    {
+        const size_t rb = (size_t)n_tok * gg.K * sizeof(uint16_t);
+        const size_t sb = engram::gathered_scratch_bytes(gg, n_tok);
+        ws += align256(rb > sb ? rb : sb);
+    }
     uint16_t* kv = (uint16_t*)ws;
     hipStream_t s = (hipStream_t)stream;
+    // the fused gather + projection where its layout applies and the tiled
+    // path runs (prefill-sized batches); gather then projection otherwise
+    const bool fused = n_tok >= 1024 && aligned16(table) && engram::gathered_supported(gg, n_tok);
     hipError_t e = engram::launch_hash(gg, *t, state, ids, B, T, hash_ids, err, s);
-    if (e == hipSuccess) e = engram::launch_gather(gg, table, scales, hash_ids, n_tok, rows, err, s);
-    if (e == hipSuccess) e = engram::launch_wkv(rows, w, n_tok, gg.N, gg.K, kv, s);
+    if (fused) {
+        if (e == hipSuccess)
+            e = engram::launch_wkv_gathered(gg, hash_ids, table, scales, w, n_tok, kv, rows, err, s);
+    } else {
+        if (e == hipSuccess)
+            e = engram::launch_gather(gg, table, scales, hash_ids, n_tok, rows, err, s);
+        if (e == hipSuccess) e = engram::launch_wkv(rows, w, n_tok, gg.N, gg.K, kv, s);
+    }
     if (e == hipSuccess) e = engram::launch_gate_add(gg, x, kv, q, k, mask, n_tok, out, gate, s);
     return from_hip(e);
 }

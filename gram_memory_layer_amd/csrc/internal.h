@@ -44,6 +44,16 @@ hipError_t launch_gather(const Geom& g, const uint8_t* table, const uint8_t* sca
 hipError_t launch_wkv(const uint16_t* a, const uint16_t* w, int64_t M, int N, int K,
                       uint16_t* kv, hipStream_t s);
 
+// number of compute units of the current device (cached)
+int cu_count();
+
+// projection straight from hash ids (rows gathered as the GEMM's A operand)
+bool gathered_supported(const Geom& g, int64_t M);
+size_t gathered_scratch_bytes(const Geom& g, int64_t M);
+hipError_t launch_wkv_gathered(const Geom& g, const int32_t* hash_ids, const uint8_t* table,
+                               const uint8_t* scales, const uint16_t* w, int64_t M, uint16_t* kv,
+                               void* scratch, uint32_t* err, hipStream_t s);
+
 hipError_t launch_gate_add(const Geom& g, const uint16_t* x, const uint16_t* kv,
                            const uint16_t* q, const uint16_t* k, const uint8_t* mask,
                            int64_t n_tok, uint16_t* out, float* gate, hipStream_t s);

@@ -21,18 +21,13 @@
 //    masked on store; no access leaves the operands.
 #include <type_traits>
 
-#include "internal.h"
+#include "tiles.h"
 
 namespace engram {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
 constexpr int BK = 64;      // k per LDS tile: 64 bf16 = 128 bytes per row
 constexpr int CH = BK / 8;  // 16-byte chunks per row
-constexpr int N_XCD = 8;    // MI355X: 8 XCDs; workgroups go round-robin over them
-constexpr int GROUP_M = 4;  // M-tiles per group in the tile order
 
 __device__ __forceinline__ int swz(int row, int ch) {
     return ch ^ ((row & 7) ^ ((row >> 3) & 1));
@@ -131,7 +126,7 @@ wkv_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, int64
         if (kt + 1 < nk) load(kt + 1);
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
-            const int ch = ks * 2 + lhalf;
+            const int ch = kchunk(ks, lhalf);
             bf16x8 fa[TM], fw[TN];
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
@@ -207,23 +202,6 @@ hipError_t run(const uint16_t* a, const uint16_t* w, int64_t M, int N, int K, ui
 constexpr int F_NT = 256;  // 4 waves in a 2 x 2 arrangement (the 8-wave variant: 512)
 constexpr bool WAVES8 = true;
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    // raw buffer: stride 0, num_records = bytes; word 3 = 0x00020000 for gfx9 data format
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                             0x00020000);
-}
-
-// 16-byte slot of logical chunk c (0..7) in a 128-byte LDS row: XOR with a
-// row function that is a permutation on any 8 consecutive rows and maps the
-// even and the odd rows of any 16 consecutive rows onto all 8 slots, so a
-// fragment read (32 consecutive rows, one logical chunk) is free of bank
-// conflicts for both 8- and 16-lane LDS issue groups.
-__device__ __forceinline__ int slot128(int row, int c) {
-    return c ^ ((row & 7) ^ ((row >> 3) & 1));
-}
-
 // BT x BT output tiles (BT = 256: 128 x 128 per wave; BT = 128: 64 x 64 per
 // wave).  Columns [0, N) of this launch start at W row 0 and C column 0; C
 // rows are `ldc` elements apart.
@@ -238,14 +216,8 @@ __device__ __forceinline__ void wkv_tile(const uint16_t* __restrict__ A,
     constexpr int NLD = BT / 8 / NW;           // LDS-bound loads per wave per operand
     constexpr int STAGE = (BM + BN) * 128;     // bytes per LDS stage
 
-    const int b = blockIdx.x;
-    const int L = (b % N_XCD) * per_xcd + b / N_XCD;
-    if (L >= tiles_m * tiles_n) return;
-    const int group_size = GROUP_M * tiles_n;
-    const int first_m = (L / group_size) * GROUP_M;
-    const int gm = min(tiles_m - first_m, GROUP_M);
-    const int mt = first_m + (L % group_size) % gm;
-    const int nt = (L % group_size) / gm;
+    int mt, nt;
+    if (!tile_of(blockIdx.x, per_xcd, tiles_m, tiles_n, &mt, &nt)) return;
     const int64_t m0 = (int64_t)mt * BM;
     const int n0 = nt * BN;
 
@@ -284,7 +256,7 @@ __device__ __forceinline__ void wkv_tile(const uint16_t* __restrict__ A,
     bf16x8 fa[2][TI], fw[2][TJ];
     auto read_frags = [&](int stage, int ks, int buf) {
         const uint8_t* st = smem + stage * STAGE;
-        const int c = ks * 2 + lhalf;
+        const int c = kchunk(ks, lhalf);
 #pragma unroll
         for (int i = 0; i < TI; ++i) {
             const int row = wm * WM + i * 32 + lrow;
@@ -468,19 +440,6 @@ hipError_t run_fast(const uint16_t* a, const uint16_t* w, int64_t M, int N, int 
     return hipGetLastError();
 }
 
-int cu_count() {
-    static int n = 0;
-    if (n == 0) {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-            v > 0)
-            n = v;
-        else
-            n = 256;
-    }
-    return n;
-}
 
 // Main path: 256 x 256 tiles over the widest column range whose tile count
 // fills whole rounds of the machine, and the remaining columns in 128 x 128
@@ -508,6 +467,20 @@ hipError_t run_main(const uint16_t* a, const uint16_t* w, int64_t M, int N, int 
 }
 
 }  // namespace
+
+int cu_count() {
+    static int n = 0;
+    if (n == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            v > 0)
+            n = v;
+        else
+            n = 256;
+    }
+    return n;
+}
 
 hipError_t launch_wkv(const uint16_t* a, const uint16_t* w, int64_t M, int N, int K,
                       uint16_t* kv, hipStream_t s) {

@@ -1,0 +1,507 @@
+// Stages 2 + 3 fused: the wkv projection with the row gather as its A loader
+// ("Module engram" docs, stages 2 and 3; the Engram block's
+// `self.wkv(self.embed(hash_ids).flatten(-2))`).
+//
+// With head_dim = 64, k-tile kt of the projection is exactly hash column kt:
+// A[m][64 kt .. 64 kt + 63] is table row hash_ids[m][kt], dequantised.  So the
+// A tile is fetched as fp8 rows straight into LDS by buffer DMA (one 64-byte
+// row per output row) and converted to bf16 only after the LDS read, with the
+// scaled fp8->bf16 convert instruction (bit-identical to the standalone
+// dequant for every value and scale code).  Compared with a materialised bf16
+// A this halves A's LDS writes and reads, drops the rows round trip through
+// HBM, and leaves room for a 3-stage ring (loads two k-tiles ahead).
+//
+// A small prep kernel first turns the hash ids into column-major arrays
+//   aoff[c][m]  byte offset of row hash_ids[m][c] in the table (or a value
+//               past the table for a bad id or a padding row: reads as 0),
+//   scl[c][m]   the row's two 32-block scales 2^(s-127) as fp32,
+// so that the projection's per-k-tile fetches are contiguous and it does no
+// id checks or scale decoding in its inner loop.
+//
+// LDS: each of the three ring stages is made of 1 KiB blocks (one buffer DMA
+// instruction each: 16 fp8 A rows, or 8 W rows of 128 bytes) plus 256 bytes
+// of scales per wave; block b of stage s sits at (3b + s) KiB within its
+// region, so a fragment's address in every stage and every fragment of a
+// wave differ by constants and the inner loop computes almost no addresses.
+// Within a block, 16-byte chunks are XOR-swizzled per row (slot64, slot128).
+// Everything else (tile order, 32x32x16 MFMA, fenced k-steps, LDS-staged
+// epilogue) is as in the bf16 kernel.
+#include <type_traits>
+
+#include "tiles.h"
+
+namespace engram {
+namespace {
+
+constexpr int G_NS = 3;                   // stages in the LDS ring
+constexpr uint32_t kBadRow = 0xFFFFFFC0u;  // >= any table's byte size: the DMA reads zeros
+
+// 16-byte slot of logical chunk c (0..3) in a 64-byte LDS row.  A fragment
+// read is one 16-byte chunk of 32 consecutive rows; the XOR term is a
+// permutation of 0..3 over the even and over the odd rows of any aligned 8
+// rows, and over each residue class mod 4 of any aligned 16 rows, so both
+// 8- and 16-lane LDS issue groups of a 128-bit read hit distinct banks.
+__device__ __forceinline__ int slot64(int row, int c) {
+    return c ^ (((row >> 1) & 3) ^ ((row >> 3) & 1));
+}
+
+// e8m0 code -> fp32 scale 2^(c-127) (code 0 is the subnormal 2^-127, 255 is NaN)
+__device__ __forceinline__ float scale_of(uint32_t c) {
+    uint32_t b = c << 23;
+    b = c == 0u ? 0x00400000u : b;
+    b = c == 0xFFu ? 0x7FC00000u : b;
+    return __uint_as_float(b);
+}
+
+// One thread per (column c, padded row m), m fastest.  Padding rows m >= M
+// get kBadRow and zero scales.
+__global__ void __launch_bounds__(256) prep_kernel(const int32_t* __restrict__ hash_ids,
+                                                   int n_cols, int64_t M, int64_t m_pad,
+                                                   const uint8_t* __restrict__ scales,
+                                                   int64_t num_rows, uint32_t* __restrict__ aoff,
+                                                   float2* __restrict__ scl,
+                                                   uint32_t* __restrict__ err) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)n_cols * m_pad) return;
+    const int c = (int)(i / m_pad);
+    const int64_t m = i - (int64_t)c * m_pad;
+    uint32_t off = kBadRow;
+    float2 sc = make_float2(0.0f, 0.0f);
+    if (m < M) {
+        const int32_t id = hash_ids[m * n_cols + c];
+        if (id >= 0 && id < num_rows) {
+            off = (uint32_t)id * 64u;
+            sc = make_float2(scale_of(scales[2 * (int64_t)id]), scale_of(scales[2 * (int64_t)id + 1]));
+        } else if (err) {
+            atomicOr(err, ENGRAM_ERRBIT_ROW);
+        }
+    }
+    aoff[i] = off;
+    scl[i] = sc;
+}
+
+// Ring hand-over: wait until at most N of this wave's vector loads are in
+// flight and its LDS reads have returned, then a workgroup barrier.  The
+// barrier is issued without a memory fence: a fence would also wait for the
+// DMA of the k-tile two ahead, which is still allowed to be in flight; the
+// "memory" clobber keeps the compiler from moving LDS accesses across it.
+template <int N>
+__device__ __forceinline__ void handover() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0070 | (N & 15) | ((N >> 4) << 14));  // vmcnt(N) lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+}
+
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+// L: the number of k-tiles after the steady loop (nk <= 2 ? nk : 3 + nk % 3),
+// a template parameter so that each kernel ends in one straight-line
+// sequence of k-tiles (branching between several leaves the register
+// allocator spilling).
+template <int BT, int WMV, int WNV, int L>
+__device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
+                                              const float2* __restrict__ scl, int n_cols,
+                                              int64_t m_pad, const uint8_t* __restrict__ table,
+                                              int64_t num_rows, const uint16_t* __restrict__ W,
+                                              int64_t M, int N, uint16_t* __restrict__ C,
+                                              int64_t ldc, int tiles_m, int tiles_n, int per_xcd,
+                                              uint8_t* smem) {
+    constexpr int NW = WMV * WNV;
+    constexpr int WM = BT / WMV, WN = BT / WNV;
+    constexpr int TI = WM / 32, TJ = WN / 32;
+    constexpr int NA = BT / 16 / NW;  // fp8 A DMA instructions per wave (16 rows each)
+    constexpr int NB = BT / 8 / NW;   // W DMA instructions per wave (8 rows each)
+    static_assert(BT / NW == 32, "one scale DMA of 32 rows per wave");
+    static_assert(NA >= 1 && NB >= 1 && TI >= 1 && TJ % 2 == 0, "tile shape");
+    constexpr int OFF_SC = (BT / 16) * G_NS * 1024;
+    constexpr int OFF_W = OFF_SC + NW * G_NS * 256;
+    constexpr int NLOAD = NA + 1 + NB;  // DMA per wave per k-tile
+    constexpr int NIDS = NA;            // row-offset loads per wave per k-tile
+
+    int mt, nt;
+    if (!tile_of(blockIdx.x, per_xcd, tiles_m, tiles_n, &mt, &nt)) return;
+    const int64_t m0 = (int64_t)mt * BT;
+    const int n0 = nt * BT;
+    const int K = n_cols * 64;
+    const int nk = n_cols;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WNV, wn = wave % WNV;
+
+    const int rows_w = min(BT, N - n0);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(aoff, (uint32_t)(n_cols * m_pad * 4));
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(scl, (uint32_t)(n_cols * m_pad * 8));
+    const __amdgpu_buffer_rsrc_t rt = make_rsrc(table, (uint32_t)(num_rows * 64));
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (int64_t)n0 * K, (uint32_t)(rows_w * K * 2));
+    const int col_o = (int)(m_pad * 4);  // aoff bytes per hash column
+    const int col_s = (int)(m_pad * 8);  // scl bytes per hash column
+
+    // DMA lanes.  fp8 A instruction i fills block NW*i + wave: rows
+    // 16*(NW*i + wave) + lane/4, lane%4 picking the 16-byte slot (which holds
+    // logical chunk slot64(row, lane%4)).  The scale instruction moves the 32
+    // rows x 2 fp32 of rows 32*wave .. 32*wave+31.  W instruction i fills
+    // block NW*i + wave: rows 8*(NW*i + wave) + lane/8.
+    uint32_t ao_v[NA], ach[NA];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+        const int row = 16 * (NW * i + wave) + (lane >> 2);
+        ao_v[i] = (uint32_t)((m0 + row) * 4);
+        ach[i] = (uint32_t)slot64(row, lane & 3) * 16u;
+    }
+    const uint32_t sc_v = (uint32_t)((m0 + 32 * wave) * 8 + lane * 4);
+    uint32_t wvoff[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const int row = (NW * i + wave) * 8 + (lane >> 3);
+        wvoff[i] = (uint32_t)(row * K * 2 + slot128(row, lane & 7) * 16);
+    }
+
+    uint32_t id_a[NA];  // table byte offsets of the next k-tile to fetch
+    auto load_offs = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < NA; ++i)
+            id_a[i] = __builtin_amdgcn_raw_buffer_load_b32(ro, ao_v[i], kt * col_o, 0);
+    };
+    auto issue_dma = [&](int kt, auto sd, const uint32_t* ia) {
+        constexpr int SD = decltype(sd)::value;
+#pragma unroll
+        for (int i = 0; i < NA; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rt, (lds_void*)(smem + ((NW * i + wave) * G_NS + SD) * 1024), 16, ia[i] + ach[i], 0,
+                0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (lds_void*)(smem + OFF_SC + (wave * G_NS + SD) * 256), 4, sc_v, kt * col_s, 0, 0);
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rw, (lds_void*)(smem + OFF_W + ((NW * i + wave) * G_NS + SD) * 1024), 16, wvoff[i],
+                kt * 128, 0, 0);
+    };
+
+    // Fragment reads.  Row wm*WM + 32i + lrow of A lies in block
+    // (wm*WM + lrow)/16 + 2i, W row wn*WN + 32j + lrow in block
+    // (wn*WN + lrow)/8 + 4j; both swizzles depend on the row mod 16 only, so
+    // one base address per lane serves every fragment and stage.  K order
+    // (kchunk): lane half h takes, over k-steps 2j' and 2j'+1, fp8 values
+    // 32j' + 16h .. +15 = logical chunk 2j' + h of its row, read once; both
+    // lie in 32-block j', whose scale comes with them.
+    const int lrow = lane & 31, lhalf = lane >> 5;
+    const int r16 = lrow & 15;
+    const uint32_t a_base =
+        (uint32_t)(((wm * WM + lrow) >> 4) * G_NS * 1024 + r16 * 64 + slot64(r16, lhalf) * 16);
+    const uint32_t s_base = (uint32_t)(OFF_SC + ((wm * WM) >> 5) * G_NS * 256 + lrow * 8);
+    const uint32_t w_base = (uint32_t)(OFF_W + ((wn * WN + lrow) >> 3) * G_NS * 1024 +
+                                       (lrow & 7) * 128 + slot128(r16, 2 * lhalf) * 16);
+
+    uint4 raw[TI];             // fp8 A: 16 values per fragment row (two k-steps)
+    float scf[TI];             // their 32-block scale
+    bf16x8 fa[TI], fw[2][TJ];  // converted A fragments, W fragments
+    auto read_a = [&](auto st, auto jc) {
+        constexpr int S = decltype(st)::value, J = decltype(jc)::value;
+        // chunk 2J + lhalf: flipping logical bit 1 flips address bit 5
+        const uint32_t ab = J ? (a_base ^ 32u) : a_base;
+#pragma unroll
+        for (int i = 0; i < TI; ++i) {
+            raw[i] = *reinterpret_cast<const uint4*>(smem + ab + i * 2 * G_NS * 1024 + S * 1024);
+            scf[i] = *reinterpret_cast<const float*>(smem + s_base + i * G_NS * 256 + S * 256 + J * 4);
+        }
+    };
+    auto read_w = [&](auto st, auto ksc, int buf) {
+        constexpr int S = decltype(st)::value, KS = decltype(ksc)::value;
+        // kchunk(KS, lhalf) = A | 2*lhalf with A = 4*(KS/2) + KS%2: XOR its
+        // bits 0 and 2 into the swizzled slot held in w_base (bits 4..6)
+        constexpr uint32_t AX = (uint32_t)(4 * (KS >> 1) + (KS & 1)) * 16u;
+        const uint32_t wb = AX ? (w_base ^ AX) : w_base;
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+            fw[buf][j] = *reinterpret_cast<const bf16x8*>(smem + wb + j * 4 * G_NS * 1024 + S * 1024);
+    };
+    // A fragment of k-step ks: the first (even ks) or second (odd ks) 8 values
+    auto convert = [&](int odd) {
+#pragma unroll
+        for (int i = 0; i < TI; ++i) {
+            const float s = scf[i];
+            const uint32_t w0 = odd ? raw[i].z : raw[i].x;
+            const uint32_t w1 = odd ? raw[i].w : raw[i].y;
+            const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, false);
+            const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, true);
+            const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, false);
+            const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, true);
+            fa[i] = __builtin_shufflevector(__builtin_shufflevector(p0, p1, 0, 1, 2, 3),
+                                            __builtin_shufflevector(p2, p3, 0, 1, 2, 3), 0, 1, 2,
+                                            3, 4, 5, 6, 7);
+        }
+    };
+
+    f32x16 acc[TJ][TI];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
+    auto mfma_half = [&](int cur, int half) {
+#pragma unroll
+        for (int j = half * (TJ / 2); j < (half + 1) * (TJ / 2); ++j)
+#pragma unroll
+            for (int i = 0; i < TI; ++i)
+                acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[cur][j], fa[i], acc[j][i],
+                                                                    0, 0, 0);
+    };
+
+    // One k-tile (in ring stage S): 4 k-steps, each converts its A fragments
+    // from the fp8 read (k-steps 0 and 2 read nothing new for A, 1 and 3 read
+    // the next pair's after converting), reads the next k-step's W fragments
+    // and issues TI*TJ MFMAs (a fenced scheduling region).  At k-step 0 the
+    // row offsets of k-tile kt+3 are loaded and the DMA of k-tile kt+2 (whose
+    // offsets arrived one k-tile ago) is issued, offsets first so that
+    // waiting for them never waits for the newer DMA.  The last k-step is
+    // split around the hand-over barrier.
+    //   WAITN: loads issued after k-tile kt+1's DMA that may stay in flight;
+    //          -1 for the last k-tile (no hand-over).
+    auto k_tile = [&](int kt, auto st, auto ldids, auto dma, auto waitn) {
+        constexpr int S = decltype(st)::value;
+        constexpr bool LOAD_IDS = decltype(ldids)::value;
+        constexpr bool DMA = decltype(dma)::value;
+        constexpr int WAITN = decltype(waitn)::value;
+        auto step = [&](auto ksc) {
+            constexpr int ks = decltype(ksc)::value;
+            constexpr int cur = ks & 1;
+            convert(cur);
+            if constexpr (ks == 0 && DMA) {
+                uint32_t ia[NA];
+#pragma unroll
+                for (int i = 0; i < NA; ++i) ia[i] = id_a[i];
+                if constexpr (LOAD_IDS) load_offs(kt + 3);
+                issue_dma(kt + 2, IC<(S + 2) % G_NS>{}, ia);
+            }
+            read_w(IC<S>{}, IC<ks + 1>{}, cur ^ 1);
+            if constexpr (ks == 1) read_a(IC<S>{}, IC<1>{});
+            mfma_half(cur, 0);
+            mfma_half(cur, 1);
+            // spread the converts, the loads of k-tile kt+2 and the fragment
+            // reads over the MFMAs so the matrix pipe never waits on issue
+#pragma unroll
+            for (int r = 0; r < TI * TJ; ++r) {
+                if (r < TI) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (ks == 0 && DMA && r < 4) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+                if (ks == 0 && DMA && r == 4) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                if (ks == 1 && r < 5) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                if (ks != 1 && r < TJ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        step(IC<0>{});
+        step(IC<1>{});
+        step(IC<2>{});
+        convert(1);
+        mfma_half(1, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (WAITN >= 0) {
+            // k-tile kt+1 is in LDS for everyone; stage S is free
+            handover<WAITN>();
+            __builtin_amdgcn_sched_barrier(0);
+            read_a(IC<(S + 1) % G_NS>{}, IC<0>{});
+            read_w(IC<(S + 1) % G_NS>{}, IC<0>{}, 0);
+        }
+        mfma_half(1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    using T = std::true_type;
+    using F = std::false_type;
+    using Wsteady = IC<NIDS + NLOAD>;
+    using W7 = IC<NLOAD>;
+    using W0 = IC<0>;
+    using Wn = IC<-1>;
+
+    // prologue: k-tiles 0 and 1 in flight, offsets of k-tile 2 loaded
+    {
+        load_offs(0);
+        uint32_t ia[NA];
+#pragma unroll
+        for (int i = 0; i < NA; ++i) ia[i] = id_a[i];
+        if (nk > 1) load_offs(1);
+        issue_dma(0, IC<0>{}, ia);
+        if (nk > 1) {
+#pragma unroll
+            for (int i = 0; i < NA; ++i) ia[i] = id_a[i];
+            if (nk > 2) load_offs(2);
+            issue_dma(1, IC<1>{}, ia);
+        }
+        if (nk > 2) handover<NIDS + NLOAD>();
+        else if (nk > 1) handover<NLOAD>();
+        else handover<0>();
+        read_a(IC<0>{}, IC<0>{});
+        read_w(IC<0>{}, IC<0>{}, 0);
+    }
+    // steady state, three k-tiles (one per stage) per iteration
+    int kt = 0;
+    for (; kt < nk - L; kt += 3) {
+        k_tile(kt, IC<0>{}, T{}, T{}, Wsteady{});
+        k_tile(kt + 1, IC<1>{}, T{}, T{}, Wsteady{});
+        k_tile(kt + 2, IC<2>{}, T{}, T{}, Wsteady{});
+    }
+    // the last L k-tiles; kt is a multiple of 3, so tile kt+p uses stage p%3
+    if constexpr (L == 1) {
+        k_tile(kt, IC<0>{}, F{}, F{}, Wn{});
+    } else if constexpr (L == 2) {
+        k_tile(kt, IC<0>{}, F{}, F{}, W0{});
+        k_tile(kt + 1, IC<1>{}, F{}, F{}, Wn{});
+    } else {
+        if constexpr (L >= 4) k_tile(kt, IC<0>{}, T{}, T{}, Wsteady{});
+        if constexpr (L == 5) k_tile(kt + 1, IC<1>{}, T{}, T{}, Wsteady{});
+        k_tile(kt + L - 3, IC<(L - 3) % G_NS>{}, F{}, T{}, W7{});
+        k_tile(kt + L - 2, IC<(L - 2) % G_NS>{}, F{}, F{}, W0{});
+        k_tile(kt + L - 1, IC<(L - 1) % G_NS>{}, F{}, F{}, Wn{});
+    }
+    __syncthreads();  // every wave is done with the ring before the epilogue reuses it
+
+    // ---- epilogue through LDS (as in the bf16 kernel)
+    constexpr int RB = WN * 2, CHW = RB / 16, RPI = 64 / CHW;
+    uint8_t* ep = smem + wave * (WM * RB);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int r = i * 32 + lrow;
+                const int nn = j * 32 + 8 * g4 + 4 * lhalf;
+                const int ch = (nn >> 3) ^ (r & (CHW - 1));
+                const uint32_t lo = f32_to_bf16(acc[j][i][4 * g4 + 0]) |
+                                    (f32_to_bf16(acc[j][i][4 * g4 + 1]) << 16);
+                const uint32_t hi = f32_to_bf16(acc[j][i][4 * g4 + 2]) |
+                                    (f32_to_bf16(acc[j][i][4 * g4 + 3]) << 16);
+                *reinterpret_cast<uint2*>(ep + r * RB + ch * 16 + (nn & 4) * 2) =
+                    make_uint2(lo, hi);
+            }
+    const int rsub = lane / CHW, csub = lane % CHW;
+#pragma unroll 4
+    for (int it = 0; it < WM / RPI; ++it) {
+        const int r = it * RPI + rsub;
+        const uint4 v =
+            *reinterpret_cast<const uint4*>(ep + r * RB + ((csub ^ (r & (CHW - 1))) << 4));
+        const int64_t m = m0 + wm * WM + r;
+        const int n = n0 + wn * WN + csub * 8;
+        if (m < M && n < N) *reinterpret_cast<uint4*>(C + m * ldc + n) = v;
+    }
+}
+
+constexpr int SMEM256 = (256 / 16) * G_NS * 1024 + 8 * G_NS * 256 + (256 / 8) * G_NS * 1024;
+constexpr int SMEM128 = (128 / 16) * G_NS * 1024 + 4 * G_NS * 256 + (128 / 8) * G_NS * 1024;
+static_assert(SMEM256 <= 160 * 1024, "LDS budget");
+static_assert(8 * 128 * 128 <= SMEM256 && 4 * 64 * 128 <= SMEM128, "epilogue staging fits the ring");
+
+template <int L>
+__global__ void __launch_bounds__(512, 1)
+wkv_gathered_256(const uint32_t* __restrict__ aoff, const float2* __restrict__ scl, int n_cols,
+                 int64_t m_pad, const uint8_t* __restrict__ table, int64_t num_rows,
+                 const uint16_t* __restrict__ W, int64_t M, int N, uint16_t* __restrict__ C,
+                 int64_t ldc, int tiles_m, int tiles_n, int per_xcd) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM256];
+    gathered_tile<256, 2, 4, L>(aoff, scl, n_cols, m_pad, table, num_rows, W, M, N, C, ldc, tiles_m,
+                             tiles_n, per_xcd, smem);
+}
+
+template <int L>
+__global__ void __launch_bounds__(256, 1)
+wkv_gathered_128(const uint32_t* __restrict__ aoff, const float2* __restrict__ scl, int n_cols,
+                 int64_t m_pad, const uint8_t* __restrict__ table, int64_t num_rows,
+                 const uint16_t* __restrict__ W, int64_t M, int N, uint16_t* __restrict__ C,
+                 int64_t ldc, int tiles_m, int tiles_n, int per_xcd) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM128];
+    gathered_tile<128, 2, 2, L>(aoff, scl, n_cols, m_pad, table, num_rows, W, M, N, C, ldc, tiles_m,
+                             tiles_n, per_xcd, smem);
+}
+
+template <int L>
+hipError_t run_gathered_l(int bt, const uint32_t* aoff, const float2* scl, int n_cols,
+                          int64_t m_pad, const uint8_t* table, int64_t num_rows,
+                          const uint16_t* w, int64_t M, int N, uint16_t* c, int64_t ldc,
+                          hipStream_t s) {
+    const int tiles_m = (int)((M + bt - 1) / bt);
+    const int tiles_n = (N + bt - 1) / bt;
+    const int total = tiles_m * tiles_n;
+    const int per_xcd = (total + N_XCD - 1) / N_XCD;
+    if (bt == 256)
+        wkv_gathered_256<L><<<dim3(per_xcd * N_XCD), dim3(512), 0, s>>>(
+            aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, tiles_m, tiles_n, per_xcd);
+    else
+        wkv_gathered_128<L><<<dim3(per_xcd * N_XCD), dim3(256), 0, s>>>(
+            aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, tiles_m, tiles_n, per_xcd);
+    return hipGetLastError();
+}
+
+hipError_t run_gathered(int bt, const uint32_t* aoff, const float2* scl, int n_cols,
+                        int64_t m_pad, const uint8_t* table, int64_t num_rows, const uint16_t* w,
+                        int64_t M, int N, uint16_t* c, int64_t ldc, hipStream_t s) {
+    const int L = n_cols <= 2 ? n_cols : 3 + n_cols % 3;
+    switch (L) {
+        case 1: return run_gathered_l<1>(bt, aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, s);
+        case 2: return run_gathered_l<2>(bt, aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, s);
+        case 3: return run_gathered_l<3>(bt, aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, s);
+        case 4: return run_gathered_l<4>(bt, aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, s);
+        default: return run_gathered_l<5>(bt, aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, s);
+    }
+}
+
+int64_t padded_rows(int64_t M) { return (M + 255) / 256 * 256; }
+
+}  // namespace
+
+// 32-bit buffer offsets: the table must stay below 4 GiB and each scratch
+// array below 2 GiB (its per-column offsets are 32-bit signed scalars)
+bool gathered_supported(const Geom& g, int64_t M) {
+    return g.head_dim == 64 && g.num_embeddings * 64 < ((int64_t)1 << 32) &&
+           (int64_t)g.n_cols * padded_rows(M) * 8 < ((int64_t)1 << 31);
+}
+
+// aoff (uint32) then scl (2 x fp32) per (hash column, padded row)
+size_t gathered_scratch_bytes(const Geom& g, int64_t M) {
+    return (size_t)g.n_cols * (size_t)padded_rows(M) * 12;
+}
+
+// Same tiling policy as the bf16 projection: 256 x 256 tiles over the widest
+// column range that fills whole rounds of the machine, 128 x 128 tiles over
+// the rest when they fit in one round.  `scratch` holds
+// gathered_scratch_bytes(g, M) bytes, 256-byte aligned.
+hipError_t launch_wkv_gathered(const Geom& g, const int32_t* hash_ids, const uint8_t* table,
+                               const uint8_t* scales, const uint16_t* w, int64_t M, uint16_t* kv,
+                               void* scratch, uint32_t* err, hipStream_t s) {
+    if (M == 0) return hipSuccess;
+    const int64_t m_pad = padded_rows(M);
+    uint32_t* aoff = reinterpret_cast<uint32_t*>(scratch);
+    float2* scl = reinterpret_cast<float2*>(aoff + (int64_t)g.n_cols * m_pad);
+    {
+        const int64_t total = (int64_t)g.n_cols * m_pad;
+        prep_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s>>>(
+            hash_ids, g.n_cols, M, m_pad, scales, g.num_embeddings, aoff, scl, err);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int N = g.N;
+    const int cus = cu_count();
+    const int tiles_m = (int)((M + 255) / 256);
+    const int tiles_n = (N + 255) / 256;
+    int nb = tiles_n;
+    if ((int64_t)tiles_m * tiles_n % cus != 0) {
+        int cand = tiles_n - 1;
+        while (cand > 0 && (int64_t)tiles_m * cand % cus != 0) --cand;
+        if (cand > 0) {
+            const int64_t small = ((M + 127) / 128) * ((N - cand * 256 + 127) / 128);
+            if (small <= cus) nb = cand;
+        }
+    }
+    const int nbig = nb * 256 < N ? nb * 256 : N;
+    hipError_t e = run_gathered(256, aoff, scl, g.n_cols, m_pad, table, g.num_embeddings, w, M,
+                                nbig, kv, N, s);
+    if (e != hipSuccess || nbig >= N) return e;
+    return run_gathered(128, aoff, scl, g.n_cols, m_pad, table, g.num_embeddings,
+                        w + (int64_t)nbig * g.K, M, N - nbig, kv + nbig, N, s);
+}
+
+}  // namespace engram

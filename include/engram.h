@@ -122,6 +122,27 @@ engram_status engram_gather(const engram_geometry* g, const uint8_t* table,
 engram_status engram_wkv(const engram_geometry* g, const uint16_t* a, const uint16_t* w,
                          int64_t M, uint16_t* kv, void* stream);
 
+/* Stages 2 and 3 fused ([docs] stages 2 and 3; [block]
+ * self.wkv(self.embed(hash_ids).flatten(-2))): the projection with the row
+ * gather as its A operand, kv = bf16( rows(hash_ids) @ w^T ), where rows is
+ * exactly what engram_gather writes (each dequantised element is the same
+ * bf16 value) and the sum is the one engram_wkv takes.  The bf16 rows never
+ * reach memory.  Requires head_dim == 64 (one table row per 64-wide k-tile)
+ * and n_hash_cols * roundup(M, 256) * 8 < 2^31; otherwise
+ * ENGRAM_ERR_UNSUPPORTED (use engram_gather + engram_wkv).
+ *   table, scales, hash_ids as in engram_gather; w, kv as in engram_wkv.
+ *   scratch  device memory of engram_wkv_gathered_scratch_size(g, M) bytes,
+ *            256-byte aligned (row offsets and scales regrouped per hash
+ *            column, 12 bytes per position and column);
+ *            contents on entry do not matter.
+ * An id outside [0, num_embeddings) reads as a zero row and sets
+ * ENGRAM_ERRBIT_ROW in *err (if err is not NULL). */
+size_t engram_wkv_gathered_scratch_size(const engram_geometry* g, int64_t M);
+engram_status engram_wkv_gathered(const engram_geometry* g, const uint8_t* table,
+                                  const uint8_t* scales, const int32_t* hash_ids, int64_t M,
+                                  const uint16_t* w, uint16_t* kv, void* scratch,
+                                  size_t scratch_bytes, uint32_t* err, void* stream);
+
 /* Stage 4: gate and add ([docs] gate_and_add; [block] forward after the
  * projection; [gate] equations for a_k and g).  Per token and stream s:
  *   w = q[s]*k[s];  rstd = rsqrt(mean(h^2)+eps) * rsqrt(mean(key^2)+eps);
@@ -138,11 +159,12 @@ engram_status engram_gate_add(const engram_geometry* g, const uint16_t* x, const
                               int64_t n_tok, uint16_t* out, float* gate, void* stream);
 
 /* Bytes of workspace engram_forward needs for n_tok = B*T positions
- * (hash ids, gathered rows and kv). */
+ * (hash ids, gathered rows or the fused projection's scratch, and kv). */
 size_t engram_forward_workspace_size(const engram_geometry* g, int64_t n_tok);
 
 /* The whole forward ([block] Engram.forward with the hash in front):
- * stage 1 -> 2 -> 3 -> 4 on one stream.  Arguments as in the stage calls;
+ * stage 1 -> 2 -> 3 -> 4 on one stream, stages 2 and 3 fused as in
+ * engram_wkv_gathered where it applies.  Arguments as in the stage calls;
  * x, out: [B, T, hc_mult, dim]; ids, mask: [B, T]; gate: [B, T, hc_mult].
  * workspace: device memory of at least engram_forward_workspace_size bytes,
  * 256-byte aligned. */

@@ -85,6 +85,34 @@ def test_host_side_rejections_launch_nothing():
     assert lib.engram_status_string(2) == b"unsupported geometry"
 
 
+def test_fused_projection_host_checks():
+    lib = ge.load()
+    g = good()
+    fake = C.c_void_p(1 << 20)
+    need = ge.engram_wkv_gathered_scratch_size(g, 4096)
+    assert need == 24 * 4096 * 12
+    assert ge.engram_wkv_gathered_scratch_size(g, 1) == 24 * 256 * 12
+
+    def call(g=g, M=16, scratch=fake, nbytes=1 << 30, table=fake):
+        return lib.engram_wkv_gathered(C.byref(g), table, fake, fake, M, fake, fake, scratch,
+                                       nbytes, None, None)
+    assert call(M=-1) == 1
+    assert call(table=None) == 1
+    assert call(table=C.c_void_p((1 << 20) + 8)) == 1    # table must be 16-byte aligned
+    assert call(scratch=None) == 3
+    assert call(nbytes=100) == 3
+    assert call(scratch=C.c_void_p((1 << 20) + 64)) == 3  # scratch must be 256-byte aligned
+    assert call(M=0) == 0
+    h = good()
+    h.head_dim = 32                                        # one row is not one k-tile
+    assert call(g=h) == 2
+    h = good()
+    h.num_embeddings = (1 << 26) + 1                       # table beyond 32-bit offsets
+    assert call(g=h) == 2
+    # small batches: the forward's workspace also holds the fused scratch
+    assert ge.engram_forward_workspace_size(g, 1) >= 256 + 24 * 256 * 12
+
+
 def test_binding_refuses_host_tensors():
     import torch
     g = good()

@@ -1,0 +1,150 @@
+"""Parity of the fused gather + projection (engram_wkv_gathered) with the
+oracle's embed_rows followed by linear, and with the library's own two-stage
+path (engram_gather then engram_wkv), which takes every product and every
+fp32 sum in the same order, so the two must agree bit for bit."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import tolerances
+from tests.gpu_util import bits, geometry, say, Workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ge():
+    import gram_memory_layer_amd as m
+    m.load()
+    return m
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return torch.device("cuda:0")
+
+
+def _small(dim, hc, max_ngram, n_heads, rows, scale_codes=(120, 132)):
+    base = synth.config("tiny")
+    return dataclasses.replace(base, dim=dim, hc_mult=hc, max_ngram_size=max_ngram,
+                               n_heads=n_heads, head_dim=64, scale_codes=scale_codes), rows
+
+
+def _check_against_oracle_and_two_stage(ge, g, cfg, table, scales, hid, w, sample=None):
+    dev = hid.device
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    kv = ge.engram_wkv_gathered(g, table, scales, hid, w, err=err)
+    two = ge.engram_wkv(g, ge.engram_gather(g, table, scales, hid), w)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert torch.equal(kv.view(torch.int16), two.view(torch.int16)), "fused != gather + wkv"
+    h = hid.reshape(-1, g.n_hash_cols).cpu().numpy()
+    pos = np.arange(h.shape[0]) if sample is None else sample
+    # the oracle sees only the table rows these positions reference
+    uniq, inv = np.unique(h[pos].reshape(-1), return_inverse=True)
+    idx = torch.from_numpy(uniq.astype(np.int64)).to(dev)
+    tab = table.index_select(0, idx).cpu().numpy()
+    sc = scales.index_select(0, idx).cpu().numpy()
+    rows = oracle.embed_rows(tab, sc, inv.reshape(len(pos), -1).astype(np.int32))
+    rows = rows.reshape(len(pos), -1)
+    wb = bits(w)
+    ref = oracle.linear(rows, wb)
+    absdot = np.abs(tolerances.bf16_value(rows)) @ np.abs(tolerances.bf16_value(wb)).T
+    got = bits(kv[torch.from_numpy(np.asarray(pos)).to(dev)])
+    return tolerances.check_kv(got, ref, absdot, g.K)
+
+
+# (dim, hc, max_ngram, n_heads): K = 64 * (max_ngram-1) * n_heads covers 1..8
+# k-tiles (every prologue and drain sequence of the 3-stage ring, with and
+# without a pass of the steady loop); N = dim*(hc+1) covers whole and ragged
+# 256- and 128-wide tiles.
+GEOMS = [(256, 3, 2, 1), (200, 4, 3, 1), (256, 1, 2, 3), (512, 2, 3, 2), (96, 4, 5, 1),
+         (128, 2, 6, 1), (320, 4, 4, 2), (64, 1, 8, 1), (256, 3, 5, 2)]
+
+
+@pytest.mark.parametrize("shape", GEOMS)
+@pytest.mark.parametrize("M", [1, 37, 300, 1100])
+def test_fused_small_geometries(ge, dev, shape, M):
+    dim, hc, mx, nh = shape
+    cfg, rows = _small(dim, hc, mx, nh, rows=5000)
+    g = geometry(ge, cfg, rows)
+    say("fused small", shape, "M", M, "N", g.N, "K", g.K)
+    table, scales = synth.embedding_table(cfg, rows, dev)
+    w = synth.wkv_weight(cfg, dev)
+    rng = np.random.default_rng(1000 * M + dim)
+    hid = torch.from_numpy(rng.integers(0, rows, (M, g.n_hash_cols)).astype(np.int32)).to(dev)
+    st = _check_against_oracle_and_two_stage(ge, g, cfg, table, scales, hid, w)
+    say("   kv", st)
+
+
+def test_fused_every_scale_code(ge, dev):
+    # all 256 e8m0 codes (NaN and the subnormal 2^-127 included) on rows that
+    # every position references; kv must match the two-stage path bit for bit
+    cfg, rows = _small(128, 1, 2, 2, rows=256)
+    g = geometry(ge, cfg, rows)
+    say("fused scale codes")
+    table, _ = synth.embedding_table(cfg, rows, dev)
+    sc = np.stack([np.arange(256), (np.arange(256) * 7 + 3) % 256], axis=1).astype(np.uint8)
+    scales = torch.from_numpy(sc).to(dev)
+    w = synth.wkv_weight(cfg, dev)
+    M = 1280
+    hid = torch.from_numpy((np.arange(M * 2) % rows).astype(np.int32).reshape(M, 2)).to(dev)
+    kv = ge.engram_wkv_gathered(g, table, scales, hid, w)
+    two = ge.engram_wkv(g, ge.engram_gather(g, table, scales, hid), w)
+    torch.cuda.synchronize()
+    assert torch.equal(kv.view(torch.int16), two.view(torch.int16))
+
+
+def test_fused_bad_ids_read_zero_rows(ge, dev):
+    cfg, rows = _small(256, 3, 3, 1, rows=3000)
+    g = geometry(ge, cfg, rows)
+    say("fused bad ids")
+    table, scales = synth.embedding_table(cfg, rows, dev)
+    w = synth.wkv_weight(cfg, dev)
+    rng = np.random.default_rng(5)
+    h = rng.integers(0, rows, (1100, g.n_hash_cols)).astype(np.int32)
+    h[3, 0], h[700, 1], h[1099, 0] = -1, rows, 1 << 30
+    hid = torch.from_numpy(h).to(dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    kv = ge.engram_wkv_gathered(g, table, scales, hid, w, err=err)
+    two = ge.engram_wkv(g, ge.engram_gather(g, table, scales, hid), w)
+    torch.cuda.synchronize()
+    assert int(err.item()) & ge.ERRBIT_ROW
+    assert torch.equal(kv.view(torch.int16), two.view(torch.int16))
+
+
+def test_fused_unsupported_head_dim(ge, dev):
+    tiny = synth.config("tiny")  # head_dim 32
+    g = geometry(ge, tiny, 100)
+    hid = torch.zeros((4, g.n_hash_cols), dtype=torch.int32, device=dev)
+    with pytest.raises(ge.EngramError):
+        ge.engram_wkv_gathered(g, torch.zeros((100, 32), dtype=torch.uint8, device=dev),
+                               torch.zeros((100, 1), dtype=torch.uint8, device=dev), hid,
+                               torch.zeros((g.N, g.K), dtype=torch.bfloat16, device=dev))
+
+
+@pytest.fixture(scope="module")
+def prefill(ge, dev):
+    return Workload(ge, "prefill", dev)
+
+
+@pytest.mark.parametrize("M", [4096, 2048, 1000])
+def test_fused_full_size(ge, dev, prefill, M):
+    # the full table (25.2 M rows) and the full 25600 x 1536 weight; hash ids
+    # uniform over the table.  Whole kv against the two-stage path, sampled
+    # rows (tile edges included) against the oracle.
+    wl = prefill
+    say("fused full M", M)
+    rng = np.random.default_rng(M)
+    hid = torch.from_numpy(rng.integers(0, wl.num_emb, (M, wl.g.n_hash_cols)).astype(np.int32))
+    hid = hid.to(dev)
+    edges = [0, 127, 128, 255, 256, M - 129, M - 128, M - 1]
+    pos = np.unique(np.concatenate([[e for e in edges if 0 <= e < M],
+                                    rng.integers(0, M, 8)]))
+    st = _check_against_oracle_and_two_stage(ge, wl.g, wl.cfg, wl.table, wl.scales, hid, wl.w,
+                                             sample=pos)
+    say("   kv", st)
