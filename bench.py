@@ -2,13 +2,15 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
-One step = one engram_forward (hash -> fp8 row gather -> wkv bf16 MFMA
-projection -> gate and add) over the DeepSeek-V4.1-shaped prefill: B=1,
-T=4096, dim=5120, hc=4, 24 hash columns of head_dim 64 (wkv 1536 -> 25600),
-a 25,160,950-row fp8 table, seeded synthetic inputs already resident in HBM.
-Prints one JSON line: whole-job tokens/s, the wkv kernel's roofline
-(flops per launch over its average launch time, measured here with HIP events
-on the stream it runs on) and the CPU oracle timed on a bounded sample.
+One step = one engram_forward (hash -> fp8 row gather fused into the wkv
+bf16 MFMA projection -> gate and add) over the DeepSeek-V4.1-shaped prefill:
+B=1, T=4096, dim=5120, hc=4, 24 hash columns of head_dim 64 (wkv 1536 ->
+25600), a 25,160,950-row fp8 table, seeded synthetic inputs already resident
+in HBM.  Prints one JSON line: whole-job tokens/s, the roofline of the
+dominant call, engram_wkv_gathered (projection flops per call over its
+average call time, measured here with HIP events on the stream it runs on;
+the call is the offset/scale prep kernel plus the two projection kernels)
+and the CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -26,7 +28,7 @@ if ROOT not in sys.path:
 METRIC = "Engram prefill tokens/s @dim5120 hc4 (1 GPU); % MFMA peak (wkv), % HBM BW (gate)"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "wkv_prefill_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "wkv_gathered_prefill_traffic.json")
 
 
 def parse():
@@ -39,20 +41,26 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run 3 plain device copies of exactly 1 GiB (a known-size kernel "
                         "against which HBM byte counters are scaled)")
+    p.add_argument("--summarize", nargs=3, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR"),
+                   help="no GPU work: turn the CSV output of three rocprofv3 runs of this "
+                        "script (--kernel-trace --stats; --pmc FETCH_SIZE; --pmc WRITE_SIZE, "
+                        "the last two with --copy-calibration) into the summaries under "
+                        "profiles/")
     return p.parse_args()
 
 
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gram_memory_layer_amd", "csrc")
-    for f in ("wkv.hip", "internal.h"):
+    for f in ("wkv_gathered.hip", "tiles.h", "internal.h"):
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
 def traffic_record(launch_flops_tokens: int):
-    """HBM bytes per wkv launch from the committed rocprofv3 counter summary,
-    or None if it was taken on a different kernel source or workload."""
+    """HBM bytes per engram_wkv_gathered call (its three kernels) from the
+    committed rocprofv3 counter summary, or None if it was taken on a
+    different kernel source or workload."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
@@ -74,8 +82,126 @@ def time_launches(fn, n, stream):
     return start.elapsed_time(end) / n * 1e-3  # seconds per launch
 
 
+# ------------------------------------------------------------------ profile summaries
+COPY_BYTES = 1 << 30
+FUSED_KERNELS = ("prep_kernel", "wkv_gathered_256", "wkv_gathered_128")
+
+
+def short_name(name: str) -> str:
+    import re
+    m = re.search(r"engram::(?:\(anonymous namespace\)::)?(\w+)(<[^>]*>)?\(", name)
+    if m:
+        return m.group(1) + (m.group(2) or "")
+    return name[:40]
+
+
+def _csv(d, suffix):
+    import csv
+    files = [f for f in os.listdir(d) if f.endswith(suffix)]
+    if len(files) != 1:
+        raise SystemExit("%s: expected one *%s, found %r" % (d, suffix, files))
+    return list(csv.DictReader(open(os.path.join(d, files[0]))))
+
+
+def _counter_means(d, counter):
+    """Mean counter value (KiB per dispatch) per engram kernel, and the value
+    for the 1 GiB calibration copy (the copy dispatch with the largest value)."""
+    per, copy = {}, 0.0
+    for r in _csv(d, "counter_collection.csv"):
+        if r["Counter_Name"] != counter:
+            continue
+        v = float(r["Counter_Value"])
+        n = r["Kernel_Name"]
+        if "engram::" in n:
+            per.setdefault(short_name(n), []).append(v)
+        elif "copy" in n.lower():
+            copy = max(copy, v)
+    if copy <= 0:
+        raise SystemExit("%s: no calibration copy dispatch (run with --copy-calibration)" % d)
+    return {k: sum(v) / len(v) for k, v in per.items()}, copy
+
+
+def summarize(stats_dir, fetch_dir, write_dir):
+    tokens = 4096
+    cmd_base = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 %s --output-format csv -d <out> -o <name> "
+                "-- python3 <repo>/bench.py --no-cpu-baseline %s")
+    # kernel-trace statistics
+    rows = _csv(stats_dir, "kernel_stats.csv")
+    lines = ["# rocprofv3 kernel-trace statistics: Engram prefill forward, T=4096, dim 5120, hc 4",
+             "# command (repository root = <repo>):",
+             "#   " + cmd_base % ("--kernel-trace --stats", ""),
+             "# engram_wkv_gathered = prep_kernel + wkv_gathered_256<L> + wkv_gathered_128<L>;",
+             "# averages include every call (warm-up and cold-clock launches too).",
+             "",
+             "%-34s %7s %12s %12s %12s %7s" % ("kernel", "calls", "avg_ns", "min_ns", "max_ns", "pct")]
+    for r in rows:
+        lines.append("%-34s %7s %12.0f %12s %12s %7s" % (
+            short_name(r["Name"]), r["Calls"], float(r["AverageNs"]), r["MinNs"], r["MaxNs"],
+            r["Percentage"]))
+    fused_avg = sum(float(r["AverageNs"]) for r in rows
+                    if short_name(r["Name"]).split("<")[0] in FUSED_KERNELS)
+    # medians from the trace: robust to the few cold-clock launches
+    durs = {}
+    for r in _csv(stats_dir, "kernel_trace.csv"):
+        k = short_name(r["Kernel_Name"])
+        if k.split("<")[0] in FUSED_KERNELS or k.startswith(("gate_kernel", "hash_kernel")):
+            durs.setdefault(k, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    med = {k: sorted(v)[len(v) // 2] for k, v in durs.items()}
+    lines.append("")
+    lines.append("# median ns per kernel (kernel trace): " +
+                 ", ".join("%s %d" % (k, v) for k, v in sorted(med.items())))
+    lines.append("# engram_wkv_gathered per call: sum of averages %.1f us, sum of medians %.1f us"
+                 % (fused_avg / 1e3,
+                    sum(v for k, v in med.items() if k.split("<")[0] in FUSED_KERNELS) / 1e3))
+    open(os.path.join(ROOT, "profiles", "engram_prefill_T4096_kernel_stats.txt"), "w").write(
+        "\n".join(lines) + "\n")
+
+    # HBM bytes from FETCH_SIZE / WRITE_SIZE, scaled by the calibration copy
+    fetch, copy_f = _counter_means(fetch_dir, "FETCH_SIZE")
+    write, copy_w = _counter_means(write_dir, "WRITE_SIZE")
+    fs = COPY_BYTES / (copy_f * 1024.0)
+    ws = COPY_BYTES / (copy_w * 1024.0)
+    lines = ["# HBM traffic per dispatch from rocprofv3 counters, Engram prefill T=4096, dim 5120, hc 4",
+             "# commands (two runs, one counter each; repository root = <repo>):",
+             "#   " + cmd_base % ("--pmc FETCH_SIZE --kernel-trace", "--steps 5 --warmup 3 --copy-calibration"),
+             "#   " + cmd_base % ("--pmc WRITE_SIZE --kernel-trace", "--steps 5 --warmup 3 --copy-calibration"),
+             "# calibration: a device copy of exactly 1 GiB reads FETCH_SIZE = %.1f KiB (scale %.4f)"
+             % (copy_f, fs),
+             "#   and WRITE_SIZE = %.1f KiB (scale %.4f)" % (copy_w, ws),
+             "# source digest of the fused projection (bench.kernel_source_digest): %s"
+             % kernel_source_digest(),
+             "",
+             "%-26s %14s %14s %12s %12s" % ("kernel", "FETCH_KiB", "WRITE_KiB", "fetch_MB*", "write_MB*")]
+    total = {"fetch": 0.0, "write": 0.0}
+    for k in sorted(set(fetch) | set(write)):
+        f, w_ = fetch.get(k, 0.0), write.get(k, 0.0)
+        lines.append("%-26s %14.1f %14.1f %12.1f %12.1f" % (k, f, w_, f * 1024 * fs / 1e6,
+                                                            w_ * 1024 * ws / 1e6))
+        if k.split("<")[0] in FUSED_KERNELS:
+            total["fetch"] += f * 1024 * fs
+            total["write"] += w_ * 1024 * ws
+    lines.append("# * scaled by the calibration copy; MB = 1e6 bytes.")
+    lines.append("# engram_wkv_gathered per call: fetch %.1f MB + write %.1f MB" %
+                 (total["fetch"] / 1e6, total["write"] / 1e6))
+    open(os.path.join(ROOT, "profiles", "engram_prefill_T4096_traffic.txt"), "w").write(
+        "\n".join(lines) + "\n")
+    rec = {"kernel": "engram_wkv_gathered (" + " + ".join(FUSED_KERNELS) + ")",
+           "workload": "prefill T=4096 dim 5120 hc 4", "tokens": tokens,
+           "source_digest": kernel_source_digest(),
+           "fetch_bytes_per_launch": int(total["fetch"]),
+           "write_bytes_per_launch": int(total["write"]),
+           "fetch_scale": fs, "write_scale": ws,
+           "hbm_bytes_per_launch": int(total["fetch"] + total["write"])}
+    json.dump(rec, open(TRAFFIC_FILE, "w"), indent=1)
+    print("wrote profiles/engram_prefill_T4096_kernel_stats.txt, "
+          "profiles/engram_prefill_T4096_traffic.txt, %s" % os.path.relpath(TRAFFIC_FILE, ROOT))
+
+
 def main():
     args = parse()
+    if args.summarize:
+        summarize(*args.summarize)
+        return
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: every box in this setup has one, and the "
               "Engram path is measured per GPU (see DESIGN.md for how it would shard).",
@@ -121,22 +247,30 @@ def main():
     wall = time.perf_counter() - t0
     tokens_per_s = n_tok / sec
 
-    # ---- per-stage launch times (each stage alone, same inputs, same stream)
+    # ---- per-stage launch times (each stage alone, same inputs, same stream);
+    # the forward runs hash -> wkv_gathered -> gate_add; gather and wkv are
+    # the unfused alternative, timed for comparison
     hid = ge.engram_hash(g, tables, ids)
     rows = ge.engram_gather(g, table, scales, hid)
     kv = ge.engram_wkv(g, rows, w)
+    scratch = torch.empty(ge.engram_wkv_gathered_scratch_size(g, n_tok), dtype=torch.uint8,
+                          device=dev)
+    ge.engram_wkv_gathered(g, table, scales, hid, w, kv=kv, scratch=scratch)
     ge.engram_gate_add(g, x, kv, q, k, mask=mask, out=out)
     torch.cuda.synchronize()
     reps = max(args.steps, 10)
     st_hash = time_launches(lambda: ge.engram_hash(g, tables, ids, hash_ids=hid), reps, stream)
     st_gather = time_launches(lambda: ge.engram_gather(g, table, scales, hid, rows=rows), reps, stream)
     st_wkv = time_launches(lambda: ge.engram_wkv(g, rows, w, kv=kv), reps, stream)
+    st_fused = time_launches(
+        lambda: ge.engram_wkv_gathered(g, table, scales, hid, w, kv=kv, scratch=scratch), reps,
+        stream)
     st_gate = time_launches(lambda: ge.engram_gate_add(g, x, kv, q, k, mask=mask, out=out), reps,
                             stream)
 
     flops_per_token = 2 * g.K * g.N
     wkv_flops = flops_per_token * n_tok
-    achieved = wkv_flops / st_wkv / 1e12
+    achieved = wkv_flops / st_fused / 1e12
     traffic = traffic_record(n_tok)
     gate_bytes = n_tok * (2 * g.hc_mult * g.dim * 2 + g.N * 2)
     rec = {
@@ -155,11 +289,15 @@ def main():
         "config": {"workload": "Engram prefill forward, B=1 T=4096, dim=5120 hc=4, 24 hash cols x "
                                "head_dim 64 (wkv 1536->25600), 25,160,950-row fp8 e4m3 table",
                    "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
-        "roofline": {"kernel": "wkv", "bound": "mfma", "achieved": round(achieved, 2),
+        "roofline": {"kernel": "engram_wkv_gathered", "bound": "mfma",
+                     "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
-        "stages_us": {"hash": round(st_hash * 1e6, 2), "gather": round(st_gather * 1e6, 2),
-                      "wkv": round(st_wkv * 1e6, 2), "gate_add": round(st_gate * 1e6, 2)},
+        "stages_us": {"hash": round(st_hash * 1e6, 2),
+                      "wkv_gathered": round(st_fused * 1e6, 2),
+                      "gate_add": round(st_gate * 1e6, 2),
+                      "unfused_gather": round(st_gather * 1e6, 2),
+                      "unfused_wkv": round(st_wkv * 1e6, 2)},
         "gate_hbm": {"achieved": round(gate_bytes / st_gate / 1e9, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(gate_bytes / st_gate / 1e9 / PEAK_HBM_GBS, 4)},
         "wall_s": round(wall, 3),
