@@ -44,13 +44,14 @@ __device__ __forceinline__ int kchunk(int ks, int h) { return 4 * (ks >> 1) + 2 
 // round-robin; the tiles of one XCD are made contiguous and ordered in
 // groups of GROUP_M M-tiles so that concurrent workgroups share A and W
 // panels in that XCD's L2.  Returns false for the padding workgroups.
+template <int GM = GROUP_M>
 __device__ __forceinline__ bool tile_of(int b, int per_xcd, int tiles_m, int tiles_n, int* mt,
                                         int* nt) {
     const int L = (b % N_XCD) * per_xcd + b / N_XCD;
     if (L >= tiles_m * tiles_n) return false;
-    const int group_size = GROUP_M * tiles_n;
-    const int first_m = (L / group_size) * GROUP_M;
-    const int gm = min(tiles_m - first_m, GROUP_M);
+    const int group_size = GM * tiles_n;
+    const int first_m = (L / group_size) * GM;
+    const int gm = min(tiles_m - first_m, GM);
     *mt = first_m + (L % group_size) % gm;
     *nt = (L % group_size) / gm;
     return true;

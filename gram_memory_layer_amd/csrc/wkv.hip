@@ -46,14 +46,8 @@ wkv_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, int64
     __shared__ uint4 lds[2][(BM + BN) * CH];
 
     // ---- tile of this workgroup
-    const int b = blockIdx.x;
-    const int L = (b % N_XCD) * per_xcd + b / N_XCD;
-    if (L >= tiles_m * tiles_n) return;
-    const int group_size = GROUP_M * tiles_n;
-    const int first_m = (L / group_size) * GROUP_M;
-    const int gm = min(tiles_m - first_m, GROUP_M);
-    const int mt = first_m + (L % group_size) % gm;
-    const int nt = (L % group_size) / gm;
+    int mt, nt;
+    if (!tile_of(blockIdx.x, per_xcd, tiles_m, tiles_n, &mt, &nt)) return;
     const int64_t m0 = (int64_t)mt * BM;
     const int n0 = nt * BN;
 

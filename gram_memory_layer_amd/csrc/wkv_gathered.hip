@@ -34,6 +34,7 @@ namespace engram {
 namespace {
 
 constexpr int G_NS = 3;                   // stages in the LDS ring
+constexpr int G_GROUP_M = 4;              // M-tiles per group in the tile order
 constexpr uint32_t kBadRow = 0xFFFFFFC0u;  // >= any table's byte size: the DMA reads zeros
 
 // 16-byte slot of logical chunk c (0..3) in a 64-byte LDS row.  A fragment
@@ -120,7 +121,7 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
     constexpr int NIDS = NA;            // row-offset loads per wave per k-tile
 
     int mt, nt;
-    if (!tile_of(blockIdx.x, per_xcd, tiles_m, tiles_n, &mt, &nt)) return;
+    if (!tile_of<G_GROUP_M>(blockIdx.x, per_xcd, tiles_m, tiles_n, &mt, &nt)) return;
     const int64_t m0 = (int64_t)mt * BT;
     const int n0 = nt * BT;
     const int K = n_cols * 64;
@@ -403,7 +404,7 @@ wkv_gathered_256(const uint32_t* __restrict__ aoff, const float2* __restrict__ s
                  const uint16_t* __restrict__ W, int64_t M, int N, uint16_t* __restrict__ C,
                  int64_t ldc, int tiles_m, int tiles_n, int per_xcd) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM256];
-    gathered_tile<256, 2, 4, L>(aoff, scl, n_cols, m_pad, table, num_rows, W, M, N, C, ldc, tiles_m,
+    gathered_tile<256, 4, 2, L>(aoff, scl, n_cols, m_pad, table, num_rows, W, M, N, C, ldc, tiles_m,
                              tiles_n, per_xcd, smem);
 }
 
