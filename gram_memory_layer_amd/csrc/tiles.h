@@ -40,6 +40,16 @@ __device__ __forceinline__ int slot128(int row, int c) {
 // form each output's sum in the same order.
 __device__ __forceinline__ int kchunk(int ks, int h) { return 4 * (ks >> 1) + 2 * h + (ks & 1); }
 
+// Two fp32 -> a packed bf16 pair (lo in the low half), round to nearest even,
+// by the hardware convert (v_cvt_pk_bf16_f32): one instruction per pair.  It
+// equals the integer rounding of f32_to_bf16 for every non-NaN input
+// (checked over all 2^32 patterns, subnormals and infinities included); a NaN
+// stays a NaN but keeps its sign and payload bits instead of becoming 0x7FC0.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
 // Workgroup b -> output tile (mt, nt).  Workgroups are dealt to the 8 XCDs
 // round-robin; the tiles of one XCD are made contiguous and ordered in
 // groups of GROUP_M M-tiles so that concurrent workgroups share A and W

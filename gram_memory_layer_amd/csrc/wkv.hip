@@ -156,10 +156,8 @@ wkv_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, int64
             for (int g4 = 0; g4 < 4; ++g4) {
                 const int n = n0 + wn * WN + j * 32 + 8 * g4 + 4 * lhalf;
                 if (n >= N) continue;
-                const uint32_t lo = f32_to_bf16(acc[j][i][4 * g4 + 0]) |
-                                    (f32_to_bf16(acc[j][i][4 * g4 + 1]) << 16);
-                const uint32_t hi = f32_to_bf16(acc[j][i][4 * g4 + 2]) |
-                                    (f32_to_bf16(acc[j][i][4 * g4 + 3]) << 16);
+                const uint32_t lo = pack_bf16(acc[j][i][4 * g4 + 0], acc[j][i][4 * g4 + 1]);
+                const uint32_t hi = pack_bf16(acc[j][i][4 * g4 + 2], acc[j][i][4 * g4 + 3]);
                 *reinterpret_cast<uint2*>(C + m * N + n) = make_uint2(lo, hi);
             }
         }
@@ -375,10 +373,8 @@ __device__ __forceinline__ void wkv_tile(const uint16_t* __restrict__ A,
                 const int r = i * 32 + lrow;
                 const int nn = j * 32 + 8 * g4 + 4 * lhalf;  // multiple of 4
                 const int ch = (nn >> 3) ^ (r & (CHW - 1));
-                const uint32_t lo = f32_to_bf16(acc[j][i][4 * g4 + 0]) |
-                                    (f32_to_bf16(acc[j][i][4 * g4 + 1]) << 16);
-                const uint32_t hi = f32_to_bf16(acc[j][i][4 * g4 + 2]) |
-                                    (f32_to_bf16(acc[j][i][4 * g4 + 3]) << 16);
+                const uint32_t lo = pack_bf16(acc[j][i][4 * g4 + 0], acc[j][i][4 * g4 + 1]);
+                const uint32_t hi = pack_bf16(acc[j][i][4 * g4 + 2], acc[j][i][4 * g4 + 3]);
                 *reinterpret_cast<uint2*>(ep + r * RB + ch * 16 + (nn & 4) * 2) =
                     make_uint2(lo, hi);
             }

@@ -115,7 +115,8 @@ engram_status engram_gather(const engram_geometry* g, const uint8_t* table,
 
 /* Stage 3: the wkv projection ([docs] stage 3, linear_bf16; [block] self.wkv):
  * kv[m][n] = bf16( sum_k a[m][k] * w[n][k] ), fp32 accumulation on bf16 MFMA,
- * no bias.
+ * no bias; the final rounding is to nearest even, and a NaN result is a NaN
+ * of unspecified sign and payload.
  *   a  bf16 [M, K];  w  bf16 [N, K] ([out, in]);  kv bf16 [M, N] out.
  * Columns [s*dim, (s+1)*dim) of kv are the key of stream s; the last dim
  * columns are the shared value. */

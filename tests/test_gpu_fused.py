@@ -96,7 +96,12 @@ def test_fused_every_scale_code(ge, dev):
     kv = ge.engram_wkv_gathered(g, table, scales, hid, w)
     two = ge.engram_wkv(g, ge.engram_gather(g, table, scales, hid), w)
     torch.cuda.synchronize()
-    assert torch.equal(kv.view(torch.int16), two.view(torch.int16))
+    # a NaN result's sign and payload are unspecified: NaN-ness must agree,
+    # everything else bit for bit
+    nan_f, nan_t = torch.isnan(kv), torch.isnan(two)
+    assert torch.equal(nan_f, nan_t)
+    assert int(nan_f.sum()) > 0 and int((~nan_f).sum()) > 0
+    assert torch.equal(kv.view(torch.int16)[~nan_f], two.view(torch.int16)[~nan_t])
 
 
 def test_fused_bad_ids_read_zero_rows(ge, dev):
