@@ -50,20 +50,27 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// Workgroup b -> output tile (mt, nt).  Workgroups are dealt to the 8 XCDs
-// round-robin; the tiles of one XCD are made contiguous and ordered in
-// groups of GROUP_M M-tiles so that concurrent workgroups share A and W
-// panels in that XCD's L2.  Returns false for the padding workgroups.
+// Tile number L (in the XCD-contiguous order) -> output tile (mt, nt): the
+// tiles are ordered in groups of GM M-tiles so that concurrent workgroups
+// share A and W panels in their XCD's L2.
 template <int GM = GROUP_M>
-__device__ __forceinline__ bool tile_of(int b, int per_xcd, int tiles_m, int tiles_n, int* mt,
-                                        int* nt) {
-    const int L = (b % N_XCD) * per_xcd + b / N_XCD;
-    if (L >= tiles_m * tiles_n) return false;
+__device__ __forceinline__ void tile_at(int L, int tiles_m, int tiles_n, int* mt, int* nt) {
     const int group_size = GM * tiles_n;
     const int first_m = (L / group_size) * GM;
     const int gm = min(tiles_m - first_m, GM);
     *mt = first_m + (L % group_size) % gm;
     *nt = (L % group_size) / gm;
+}
+
+// Workgroup b -> output tile (mt, nt).  Workgroups are dealt to the 8 XCDs
+// round-robin; each XCD takes a contiguous range of per_xcd tile numbers.
+// Returns false for the padding workgroups.
+template <int GM = GROUP_M>
+__device__ __forceinline__ bool tile_of(int b, int per_xcd, int tiles_m, int tiles_n, int* mt,
+                                        int* nt) {
+    const int L = (b % N_XCD) * per_xcd + b / N_XCD;
+    if (L >= tiles_m * tiles_n) return false;
+    tile_at<GM>(L, tiles_m, tiles_n, mt, nt);
     return true;
 }
 

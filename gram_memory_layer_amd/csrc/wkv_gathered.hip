@@ -96,11 +96,19 @@ __device__ __forceinline__ void handover() {
 template <int V>
 using IC = std::integral_constant<int, V>;
 
-// L: the number of k-tiles after the steady loop (nk <= 2 ? nk : 3 + nk % 3),
-// a template parameter so that each kernel ends in one straight-line
-// sequence of k-tiles (branching between several leaves the register
-// allocator spilling).
-template <int BT, int WMV, int WNV, int L>
+// One workgroup's work.
+//   P = false: one output tile; L is the number of k-tiles after the steady
+//     loop (nk <= 2 ? nk : 3 + nk % 3), a template parameter so that each
+//     kernel ends in one straight-line sequence of k-tiles (branching between
+//     several leaves the register allocator spilling).
+//   P = true (persistent): a sequence of tiles, every one full-width in N and
+//     nk a multiple of 3.  The k-tile pipeline runs on across tiles: the
+//     last k-tiles of a tile already load the first ones of the next, and a
+//     tile's output is staged through the ring stage that is free at that
+//     point, so neither the start-up latency of a tile nor its stores stall
+//     the matrix pipe for long.  The last tile loads its own first k-tiles a
+//     second time (harmless; they land before the workgroup ends).
+template <int BT, int WMV, int WNV, int L, bool P>
 __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
                                               const float2* __restrict__ scl, int n_cols,
                                               int64_t m_pad, const uint8_t* __restrict__ table,
@@ -120,23 +128,53 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
     constexpr int NLOAD = NA + 1 + NB;  // DMA per wave per k-tile
     constexpr int NIDS = NA;            // row-offset loads per wave per k-tile
 
-    int mt, nt;
-    if (!tile_of<G_GROUP_M>(blockIdx.x, per_xcd, tiles_m, tiles_n, &mt, &nt)) return;
-    const int64_t m0 = (int64_t)mt * BT;
-    const int n0 = nt * BT;
     const int K = n_cols * 64;
     const int nk = n_cols;
+    // current tile (m0c, n0c) and the next one of this workgroup (itself at
+    // the end of the sequence)
+    const int xcd = blockIdx.x % N_XCD, slot = blockIdx.x / N_XCD;
+    const int nwg = gridDim.x / N_XCD;
+    auto tile_valid = [&](int q) {
+        const int idx = slot + q * nwg;
+        return idx < per_xcd && xcd * per_xcd + idx < tiles_m * tiles_n;
+    };
+    int m0c, n0c, m0n, n0n;
+    {
+        int mt, nt;
+        if constexpr (P) {
+            if (!tile_valid(0)) return;
+            tile_at<G_GROUP_M>(xcd * per_xcd + slot, tiles_m, tiles_n, &mt, &nt);
+        } else {
+            if (!tile_of<G_GROUP_M>(blockIdx.x, per_xcd, tiles_m, tiles_n, &mt, &nt)) return;
+        }
+        m0c = m0n = mt * BT;
+        n0c = n0n = nt * BT;
+    }
+    auto set_next = [&](int q) {
+        if (tile_valid(q)) {
+            int mt, nt;
+            tile_at<G_GROUP_M>(xcd * per_xcd + slot + q * nwg, tiles_m, tiles_n, &mt, &nt);
+            m0n = mt * BT;
+            n0n = nt * BT;
+        } else {
+            m0n = m0c;
+            n0n = n0c;
+        }
+    };
+    if constexpr (P) set_next(1);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WNV, wn = wave % WNV;
 
-    const int rows_w = min(BT, N - n0);
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(aoff, (uint32_t)(n_cols * m_pad * 4));
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(scl, (uint32_t)(n_cols * m_pad * 8));
     const __amdgpu_buffer_rsrc_t rt = make_rsrc(table, (uint32_t)(num_rows * 64));
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (int64_t)n0 * K, (uint32_t)(rows_w * K * 2));
+    // W rows n0 .. n0+BT-1 (rows past N read as zeros)
+    auto w_rsrc = [&](int n0x) {
+        return make_rsrc(W + (int64_t)n0x * K, (uint32_t)(min(BT, N - n0x) * K * 2));
+    };
     const int col_o = (int)(m_pad * 4);  // aoff bytes per hash column
     const int col_s = (int)(m_pad * 8);  // scl bytes per hash column
 
@@ -149,10 +187,10 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
         const int row = 16 * (NW * i + wave) + (lane >> 2);
-        ao_v[i] = (uint32_t)((m0 + row) * 4);
+        ao_v[i] = (uint32_t)(row * 4);  // + m0*4 in the scalar offset
         ach[i] = (uint32_t)slot64(row, lane & 3) * 16u;
     }
-    const uint32_t sc_v = (uint32_t)((m0 + 32 * wave) * 8 + lane * 4);
+    const uint32_t sc_v = (uint32_t)(32 * wave * 8 + lane * 4);  // + m0*8 likewise
     uint32_t wvoff[NB];
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
@@ -161,20 +199,22 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
     }
 
     uint32_t id_a[NA];  // table byte offsets of the next k-tile to fetch
-    auto load_offs = [&](int kt) {
+    auto load_offs = [&](int kt, int m0x) {
 #pragma unroll
         for (int i = 0; i < NA; ++i)
-            id_a[i] = __builtin_amdgcn_raw_buffer_load_b32(ro, ao_v[i], kt * col_o, 0);
+            id_a[i] = __builtin_amdgcn_raw_buffer_load_b32(ro, ao_v[i], kt * col_o + m0x * 4, 0);
     };
-    auto issue_dma = [&](int kt, auto sd, const uint32_t* ia) {
+    auto issue_dma = [&](int kt, auto sd, const uint32_t* ia, int m0x, int n0x) {
         constexpr int SD = decltype(sd)::value;
+        const __amdgpu_buffer_rsrc_t rw = w_rsrc(n0x);
 #pragma unroll
         for (int i = 0; i < NA; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rt, (lds_void*)(smem + ((NW * i + wave) * G_NS + SD) * 1024), 16, ia[i] + ach[i], 0,
                 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (lds_void*)(smem + OFF_SC + (wave * G_NS + SD) * 256), 4, sc_v, kt * col_s, 0, 0);
+            rs, (lds_void*)(smem + OFF_SC + (wave * G_NS + SD) * 256), 4, sc_v,
+            kt * col_s + m0x * 8, 0, 0);
 #pragma unroll
         for (int i = 0; i < NB; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -276,8 +316,11 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
                 uint32_t ia[NA];
 #pragma unroll
                 for (int i = 0; i < NA; ++i) ia[i] = id_a[i];
-                if constexpr (LOAD_IDS) load_offs(kt + 3);
-                issue_dma(kt + 2, IC<(S + 2) % G_NS>{}, ia);
+                // persistent: past this tile's last k-tile, load the next tile's
+                const bool nx3 = P && kt + 3 >= nk, nx2 = P && kt + 2 >= nk;
+                if constexpr (LOAD_IDS) load_offs(nx3 ? kt + 3 - nk : kt + 3, nx3 ? m0n : m0c);
+                issue_dma(nx2 ? kt + 2 - nk : kt + 2, IC<(S + 2) % G_NS>{}, ia, nx2 ? m0n : m0c,
+                          nx2 ? n0n : n0c);
             }
             read_w(IC<S>{}, IC<ks + 1>{}, cur ^ 1);
             if constexpr (ks == 1) read_a(IC<S>{}, IC<1>{});
@@ -321,17 +364,17 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
 
     // prologue: k-tiles 0 and 1 in flight, offsets of k-tile 2 loaded
     {
-        load_offs(0);
+        load_offs(0, m0c);
         uint32_t ia[NA];
 #pragma unroll
         for (int i = 0; i < NA; ++i) ia[i] = id_a[i];
-        if (nk > 1) load_offs(1);
-        issue_dma(0, IC<0>{}, ia);
+        if (nk > 1) load_offs(1, m0c);
+        issue_dma(0, IC<0>{}, ia, m0c, n0c);
         if (nk > 1) {
 #pragma unroll
             for (int i = 0; i < NA; ++i) ia[i] = id_a[i];
-            if (nk > 2) load_offs(2);
-            issue_dma(1, IC<1>{}, ia);
+            if (nk > 2) load_offs(2, m0c);
+            issue_dma(1, IC<1>{}, ia, m0c, n0c);
         }
         if (nk > 2) handover<NIDS + NLOAD>();
         else if (nk > 1) handover<NLOAD>();
@@ -339,54 +382,126 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
         read_a(IC<0>{}, IC<0>{});
         read_w(IC<0>{}, IC<0>{}, 0);
     }
-    // steady state, three k-tiles (one per stage) per iteration
-    int kt = 0;
-    for (; kt < nk - L; kt += 3) {
-        k_tile(kt, IC<0>{}, T{}, T{}, Wsteady{});
-        k_tile(kt + 1, IC<1>{}, T{}, T{}, Wsteady{});
-        k_tile(kt + 2, IC<2>{}, T{}, T{}, Wsteady{});
-    }
-    // the last L k-tiles; kt is a multiple of 3, so tile kt+p uses stage p%3
-    if constexpr (L == 1) {
-        k_tile(kt, IC<0>{}, F{}, F{}, Wn{});
-    } else if constexpr (L == 2) {
-        k_tile(kt, IC<0>{}, F{}, F{}, W0{});
-        k_tile(kt + 1, IC<1>{}, F{}, F{}, Wn{});
-    } else {
-        if constexpr (L >= 4) k_tile(kt, IC<0>{}, T{}, T{}, Wsteady{});
-        if constexpr (L == 5) k_tile(kt + 1, IC<1>{}, T{}, T{}, Wsteady{});
-        k_tile(kt + L - 3, IC<(L - 3) % G_NS>{}, F{}, T{}, W7{});
-        k_tile(kt + L - 2, IC<(L - 2) % G_NS>{}, F{}, F{}, W0{});
-        k_tile(kt + L - 1, IC<(L - 1) % G_NS>{}, F{}, F{}, Wn{});
-    }
-    __syncthreads();  // every wave is done with the ring before the epilogue reuses it
-
-    // ---- epilogue through LDS (as in the bf16 kernel)
-    constexpr int RB = WN * 2, CHW = RB / 16, RPI = 64 / CHW;
-    uint8_t* ep = smem + wave * (WM * RB);
+    if constexpr (P) {
+        // Output of the tile just finished, staged through ring stage 2: once
+        // every wave is past the hand-over of the tile's last k-tile (stage
+        // 2), stage 2 is unused until the next tile's first k-tile refills
+        // it, while stages 0 and 1 hold or receive the next tile's first two
+        // k-tiles.  Its 1 KiB blocks give each wave PB private blocks, two per
+        // 32x32 fragment (16 rows of 64 bytes each), so the fragments go out
+        // in passes of PB/2 with no workgroup barrier in between.
+        constexpr int NBLK = BT / 16 + BT / 8;
+        constexpr int PB = NBLK / NW, FP = PB / 2, NF = TI * TJ;
+        static_assert(NBLK % NW == 0 && FP >= 1, "staging blocks");
+        auto blk = [&](int q) -> uint32_t {  // this wave's staging block q (0 .. PB-1)
+            const int gq = wave * PB + q;
+            return gq < BT / 16 ? (uint32_t)((gq * G_NS + 2) * 1024)
+                                : (uint32_t)(OFF_W + ((gq - BT / 16) * G_NS + 2) * 1024);
+        };
+        auto epilogue = [&]() {
 #pragma unroll
-    for (int j = 0; j < TJ; ++j)
+            for (int f0 = 0; f0 < NF; f0 += FP) {
 #pragma unroll
-        for (int i = 0; i < TI; ++i)
+                for (int s = 0; s < FP; ++s) {
+                    if (f0 + s >= NF) break;
+                    const int j = (f0 + s) / TI, i = (f0 + s) % TI;
+                    const uint32_t b = blk(2 * s + (lrow >> 4)) + (lrow & 15) * 64 + lhalf * 8;
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int r = i * 32 + lrow;
-                const int nn = j * 32 + 8 * g4 + 4 * lhalf;
-                const int ch = (nn >> 3) ^ (r & (CHW - 1));
-                const uint32_t lo = pack_bf16(acc[j][i][4 * g4 + 0], acc[j][i][4 * g4 + 1]);
-                const uint32_t hi = pack_bf16(acc[j][i][4 * g4 + 2], acc[j][i][4 * g4 + 3]);
-                *reinterpret_cast<uint2*>(ep + r * RB + ch * 16 + (nn & 4) * 2) =
-                    make_uint2(lo, hi);
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const uint32_t lo = pack_bf16(acc[j][i][4 * g4 + 0], acc[j][i][4 * g4 + 1]);
+                        const uint32_t hi = pack_bf16(acc[j][i][4 * g4 + 2], acc[j][i][4 * g4 + 3]);
+                        *reinterpret_cast<uint2*>(smem + b + ((g4 ^ (lrow & 3)) << 4)) =
+                            make_uint2(lo, hi);
+                    }
+                }
+#pragma unroll
+                for (int s = 0; s < FP; ++s) {
+                    if (f0 + s >= NF) break;
+                    const int j = (f0 + s) / TI, i = (f0 + s) % TI;
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int rr = (lane >> 2) + 16 * hh, sl = lane & 3;
+                        const uint4 v = *reinterpret_cast<const uint4*>(
+                            smem + blk(2 * s + hh) + (rr & 15) * 64 + sl * 16);
+                        const int64_t m = (int64_t)m0c + wm * WM + i * 32 + rr;
+                        const int n = n0c + wn * WN + j * 32 + ((sl ^ (rr & 3)) << 3);
+                        if (m < M && n < N) *reinterpret_cast<uint4*>(C + m * ldc + n) = v;
+                    }
+                }
             }
-    const int rsub = lane / CHW, csub = lane % CHW;
+            __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0): staging reads returned
+            asm volatile("s_barrier" ::: "memory");  // stage 2 free for the next DMA
+        };
+        for (int q = 1;; ++q) {
+            for (int kt = 0; kt < nk; kt += 3) {
+                k_tile(kt, IC<0>{}, T{}, T{}, Wsteady{});
+                k_tile(kt + 1, IC<1>{}, T{}, T{}, Wsteady{});
+                k_tile(kt + 2, IC<2>{}, T{}, T{}, Wsteady{});
+            }
+            epilogue();
+            if (!tile_valid(q)) break;
+            m0c = m0n;
+            n0c = n0n;
+            set_next(q + 1);
+#pragma unroll
+            for (int j = 0; j < TJ; ++j)
+#pragma unroll
+                for (int i = 0; i < TI; ++i)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no DMA into LDS left at exit
+        return;
+    } else {
+        // steady state, three k-tiles (one per stage) per iteration
+        int kt = 0;
+        for (; kt < nk - L; kt += 3) {
+            k_tile(kt, IC<0>{}, T{}, T{}, Wsteady{});
+            k_tile(kt + 1, IC<1>{}, T{}, T{}, Wsteady{});
+            k_tile(kt + 2, IC<2>{}, T{}, T{}, Wsteady{});
+        }
+        // the last L k-tiles; kt is a multiple of 3, so tile kt+p uses stage p%3
+        if constexpr (L == 1) {
+            k_tile(kt, IC<0>{}, F{}, F{}, Wn{});
+        } else if constexpr (L == 2) {
+            k_tile(kt, IC<0>{}, F{}, F{}, W0{});
+            k_tile(kt + 1, IC<1>{}, F{}, F{}, Wn{});
+        } else {
+            if constexpr (L >= 4) k_tile(kt, IC<0>{}, T{}, T{}, Wsteady{});
+            if constexpr (L == 5) k_tile(kt + 1, IC<1>{}, T{}, T{}, Wsteady{});
+            k_tile(kt + L - 3, IC<(L - 3) % G_NS>{}, F{}, T{}, W7{});
+            k_tile(kt + L - 2, IC<(L - 2) % G_NS>{}, F{}, F{}, W0{});
+            k_tile(kt + L - 1, IC<(L - 1) % G_NS>{}, F{}, F{}, Wn{});
+        }
+        __syncthreads();  // every wave is done with the ring before the epilogue reuses it
+
+        // ---- epilogue through LDS (as in the bf16 kernel)
+        constexpr int RB = WN * 2, CHW = RB / 16, RPI = 64 / CHW;
+        uint8_t* ep = smem + wave * (WM * RB);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+            for (int i = 0; i < TI; ++i)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int r = i * 32 + lrow;
+                    const int nn = j * 32 + 8 * g4 + 4 * lhalf;
+                    const int ch = (nn >> 3) ^ (r & (CHW - 1));
+                    const uint32_t lo = pack_bf16(acc[j][i][4 * g4 + 0], acc[j][i][4 * g4 + 1]);
+                    const uint32_t hi = pack_bf16(acc[j][i][4 * g4 + 2], acc[j][i][4 * g4 + 3]);
+                    *reinterpret_cast<uint2*>(ep + r * RB + ch * 16 + (nn & 4) * 2) =
+                        make_uint2(lo, hi);
+                }
+        const int rsub = lane / CHW, csub = lane % CHW;
 #pragma unroll 4
-    for (int it = 0; it < WM / RPI; ++it) {
-        const int r = it * RPI + rsub;
-        const uint4 v =
-            *reinterpret_cast<const uint4*>(ep + r * RB + ((csub ^ (r & (CHW - 1))) << 4));
-        const int64_t m = m0 + wm * WM + r;
-        const int n = n0 + wn * WN + csub * 8;
-        if (m < M && n < N) *reinterpret_cast<uint4*>(C + m * ldc + n) = v;
+        for (int it = 0; it < WM / RPI; ++it) {
+            const int r = it * RPI + rsub;
+            const uint4 v =
+                *reinterpret_cast<const uint4*>(ep + r * RB + ((csub ^ (r & (CHW - 1))) << 4));
+            const int64_t m = (int64_t)m0c + wm * WM + r;
+            const int n = n0c + wn * WN + csub * 8;
+            if (m < M && n < N) *reinterpret_cast<uint4*>(C + m * ldc + n) = v;
+        }
     }
 }
 
@@ -395,15 +510,15 @@ constexpr int SMEM128 = (128 / 16) * G_NS * 1024 + 4 * G_NS * 256 + (128 / 8) * 
 static_assert(SMEM256 <= 160 * 1024, "LDS budget");
 static_assert(8 * 128 * 128 <= SMEM256 && 4 * 64 * 128 <= SMEM128, "epilogue staging fits the ring");
 
-template <int L>
+template <int L, bool P>
 __global__ void __launch_bounds__(512, 1)
 wkv_gathered_256(const uint32_t* __restrict__ aoff, const float2* __restrict__ scl, int n_cols,
                  int64_t m_pad, const uint8_t* __restrict__ table, int64_t num_rows,
                  const uint16_t* __restrict__ W, int64_t M, int N, uint16_t* __restrict__ C,
                  int64_t ldc, int tiles_m, int tiles_n, int per_xcd) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM256];
-    gathered_tile<256, 4, 2, L>(aoff, scl, n_cols, m_pad, table, num_rows, W, M, N, C, ldc, tiles_m,
-                             tiles_n, per_xcd, smem);
+    gathered_tile<256, 4, 2, L, P>(aoff, scl, n_cols, m_pad, table, num_rows, W, M, N, C, ldc,
+                                   tiles_m, tiles_n, per_xcd, smem);
 }
 
 template <int L>
@@ -413,8 +528,8 @@ wkv_gathered_128(const uint32_t* __restrict__ aoff, const float2* __restrict__ s
                  const uint16_t* __restrict__ W, int64_t M, int N, uint16_t* __restrict__ C,
                  int64_t ldc, int tiles_m, int tiles_n, int per_xcd) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM128];
-    gathered_tile<128, 2, 2, L>(aoff, scl, n_cols, m_pad, table, num_rows, W, M, N, C, ldc, tiles_m,
-                             tiles_n, per_xcd, smem);
+    gathered_tile<128, 2, 2, L, false>(aoff, scl, n_cols, m_pad, table, num_rows, W, M, N, C, ldc,
+                                       tiles_m, tiles_n, per_xcd, smem);
 }
 
 template <int L>
@@ -427,7 +542,7 @@ hipError_t run_gathered_l(int bt, const uint32_t* aoff, const float2* scl, int n
     const int total = tiles_m * tiles_n;
     const int per_xcd = (total + N_XCD - 1) / N_XCD;
     if (bt == 256)
-        wkv_gathered_256<L><<<dim3(per_xcd * N_XCD), dim3(512), 0, s>>>(
+        wkv_gathered_256<L, false><<<dim3(per_xcd * N_XCD), dim3(512), 0, s>>>(
             aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, tiles_m, tiles_n, per_xcd);
     else
         wkv_gathered_128<L><<<dim3(per_xcd * N_XCD), dim3(256), 0, s>>>(
@@ -446,6 +561,23 @@ hipError_t run_gathered(int bt, const uint32_t* aoff, const float2* scl, int n_c
         case 4: return run_gathered_l<4>(bt, aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, s);
         default: return run_gathered_l<5>(bt, aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, s);
     }
+}
+
+// Persistent 256x256 launch: one workgroup per compute unit (a multiple of 8,
+// so every XCD gets the same number), each running its XCD's tiles
+// slot, slot + nwg, ...  Needs nk % 3 == 0 and N a multiple of 256.
+hipError_t run_persistent(const uint32_t* aoff, const float2* scl, int n_cols, int64_t m_pad,
+                          const uint8_t* table, int64_t num_rows, const uint16_t* w, int64_t M,
+                          int N, uint16_t* c, int64_t ldc, int cus, hipStream_t s) {
+    const int tiles_m = (int)((M + 255) / 256);
+    const int tiles_n = N / 256;
+    const int total = tiles_m * tiles_n;
+    const int per_xcd = (total + N_XCD - 1) / N_XCD;
+    int grid = cus / N_XCD * N_XCD;
+    if (grid > per_xcd * N_XCD) grid = per_xcd * N_XCD;
+    wkv_gathered_256<3, true><<<dim3(grid), dim3(512), 0, s>>>(
+        aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, tiles_m, tiles_n, per_xcd);
+    return hipGetLastError();
 }
 
 int64_t padded_rows(int64_t M) { return (M + 255) / 256 * 256; }
@@ -496,8 +628,14 @@ hipError_t launch_wkv_gathered(const Geom& g, const int32_t* hash_ids, const uin
         }
     }
     const int nbig = nb * 256 < N ? nb * 256 : N;
-    hipError_t e = run_gathered(256, aoff, scl, g.n_cols, m_pad, table, g.num_embeddings, w, M,
-                                nbig, kv, N, s);
+    hipError_t e;
+    if (g.n_cols % 3 == 0 && nbig % 256 == 0 && cus >= N_XCD &&
+        (int64_t)tiles_m * (nbig / 256) >= 2 * cus)
+        e = run_persistent(aoff, scl, g.n_cols, m_pad, table, g.num_embeddings, w, M, nbig, kv, N,
+                           cus, s);
+    else
+        e = run_gathered(256, aoff, scl, g.n_cols, m_pad, table, g.num_embeddings, w, M, nbig, kv,
+                         N, s);
     if (e != hipSuccess || nbig >= N) return e;
     return run_gathered(128, aoff, scl, g.n_cols, m_pad, table, g.num_embeddings,
                         w + (int64_t)nbig * g.K, M, N - nbig, kv + nbig, N, s);

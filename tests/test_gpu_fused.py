@@ -81,6 +81,25 @@ def test_fused_small_geometries(ge, dev, shape, M):
     say("   kv", st)
 
 
+# Shapes that take the persistent 256x256 kernel (nk % 3 == 0 and at least two
+# tiles per compute unit): nk = 3 and 6, an uneven number of tiles per
+# workgroup, and a ragged last M-tile.
+@pytest.mark.parametrize("dim,hc,mx,nh,M", [(2048, 4, 2, 3, 4096), (2048, 4, 3, 3, 4000),
+                                            (1024, 4, 4, 2, 8192)])
+def test_fused_persistent_shapes(ge, dev, dim, hc, mx, nh, M):
+    cfg, rows = _small(dim, hc, mx, nh, rows=100000)
+    g = geometry(ge, cfg, rows)
+    say("fused persistent", (dim, hc, mx, nh), "M", M, "N", g.N, "K", g.K)
+    table, scales = synth.embedding_table(cfg, rows, dev)
+    w = synth.wkv_weight(cfg, dev)
+    rng = np.random.default_rng(M + dim)
+    hid = torch.from_numpy(rng.integers(0, rows, (M, g.n_hash_cols)).astype(np.int32)).to(dev)
+    pos = np.unique(np.concatenate([[0, 255, 256, M - 257, M - 256, M - 1],
+                                    rng.integers(0, M, 10)]))
+    st = _check_against_oracle_and_two_stage(ge, g, cfg, table, scales, hid, w, sample=pos)
+    say("   kv", st)
+
+
 def test_fused_every_scale_code(ge, dev):
     # all 256 e8m0 codes (NaN and the subnormal 2^-127 included) on rows that
     # every position references; kv must match the two-stage path bit for bit
