@@ -195,6 +195,20 @@ engram_status engram_forward(const engram_geometry* g, const engram_hash_tables*
     // path runs (prefill-sized batches); gather then projection otherwise
     const bool fused = n_tok >= 1024 && aligned16(table) && engram::gathered_supported(gg, n_tok);
     hipError_t e = engram::launch_hash(gg, *t, state, ids, B, T, hash_ids, err, s);
+    if (fused && engram::gate_partials_supported(gg, n_tok)) {
+        // fully fused: the projection reduces the key columns into the gate's
+        // partial sums and stores only the value; kv's region holds both
+        uint16_t* v = kv;
+        float2* part = reinterpret_cast<float2*>(
+            reinterpret_cast<char*>(kv) + align256((size_t)n_tok * gg.dim * sizeof(uint16_t)));
+        const engram::GatePartials gp{x, q, k, part, gg.dim, gg.hc};
+        if (e == hipSuccess)
+            e = engram::launch_wkv_gate_partials(gg, hash_ids, table, scales, w, n_tok, gp, v,
+                                                 rows, err, s);
+        if (e == hipSuccess)
+            e = engram::launch_gate_from_partials(gg, x, v, part, mask, n_tok, out, gate, s);
+        return from_hip(e);
+    }
     if (fused) {
         if (e == hipSuccess)
             e = engram::launch_wkv_gathered(gg, hash_ids, table, scales, w, n_tok, kv, rows, err, s);

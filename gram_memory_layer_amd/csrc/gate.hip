@@ -1,6 +1,8 @@
 // Stage 4: gate and add ("Module engram" docs, gate_and_add; the Engram
 // block's forward after the projection; "Gate per stream" equations for a_k
-// and g).
+// and g).  Two forms: from the full kv (keys and value), or, in the fully
+// fused prefill, from the value alone plus the key-side partial sums the
+// projection's epilogue produced (S_kk and S_hwk per 128 columns).
 //
 // One workgroup per token.  Each thread owns NCH 16-byte chunks (8 features)
 // of every stream and of the shared value: it loads them once, keeps x and
@@ -43,14 +45,17 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-template <int HC, int NCH>
+// PART: the key-side sums come as per-128-column partials from the
+// projection's epilogue (kv then points at the value [n_tok, dim] alone, q and
+// kw are unused); only S_hh is reduced here.
+template <int HC, int NCH, bool PART>
 __global__ void __launch_bounds__(1024) gate_kernel(
     const uint16_t* x, const uint16_t* __restrict__ kv,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kw,
-    const uint8_t* __restrict__ mask, int dim, float eps, float inv_sqrt_dim,
-    uint16_t* out, float* __restrict__ gate) {
+    const float2* __restrict__ part, const uint8_t* __restrict__ mask, int dim, float eps,
+    float inv_sqrt_dim, uint16_t* out, float* __restrict__ gate) {
 #pragma clang fp contract(off)
-    constexpr int NS = 3 * HC;
+    constexpr int NS = PART ? HC : 3 * HC;
     __shared__ float red[16][NS];
     __shared__ float gsh[HC];
 
@@ -58,7 +63,8 @@ __global__ void __launch_bounds__(1024) gate_kernel(
     const int tid = threadIdx.x;
     const int nthr = blockDim.x;
     const int d8 = dim / 8;
-    const int64_t row = (int64_t)dim * (HC + 1);
+    const int64_t row = PART ? (int64_t)dim : (int64_t)dim * (HC + 1);
+    const int64_t voff = PART ? 0 : (int64_t)HC * dim;  // value within the kv row
     const uint16_t* xt = x + tok * HC * dim;
     const uint16_t* kvt = kv + tok * row;
     uint16_t* ot = out + tok * HC * dim;
@@ -85,6 +91,15 @@ __global__ void __launch_bounds__(1024) gate_kernel(
         return;
     }
 
+    // PART: the token's HC * dim/128 partial pairs are fetched first, one per
+    // thread, into LDS, so their latency overlaps the x loads; they are
+    // summed in order after the block reduction
+    __shared__ float2 psh[PART ? HC * 256 : 1];
+    if constexpr (PART) {
+        const int np = HC * (dim >> 7);  // dim <= 32768: at most HC * 256 pairs
+        for (int t = tid; t < np; t += nthr) psh[t] = part[tok * np + t];
+    }
+
     float acc[NS];
 #pragma unroll
     for (int j = 0; j < NS; ++j) acc[j] = 0.0f;
@@ -93,32 +108,42 @@ __global__ void __launch_bounds__(1024) gate_kernel(
     for (int i = 0; i < NCH; ++i) {
         const int c = tid + i * nthr;
         if (c < d8) {
-            if (KEEP) vr[i < KC ? i : 0] = *reinterpret_cast<const uint4*>(kvt + (int64_t)HC * dim + c * 8);
+            if (KEEP) vr[i < KC ? i : 0] = *reinterpret_cast<const uint4*>(kvt + voff + c * 8);
 #pragma unroll
             for (int s = 0; s < HC; ++s) {
                 const uint4 h = *reinterpret_cast<const uint4*>(xt + (int64_t)s * dim + c * 8);
-                const uint4 key = *reinterpret_cast<const uint4*>(kvt + (int64_t)s * dim + c * 8);
-                const uint4 qq = *reinterpret_cast<const uint4*>(q + (int64_t)s * dim + c * 8);
-                const uint4 kk = *reinterpret_cast<const uint4*>(kw + (int64_t)s * dim + c * 8);
                 if (KEEP) xr[s][i < KC ? i : 0] = h;
-                const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
-                const uint32_t kyw[4] = {key.x, key.y, key.z, key.w};
-                const uint32_t qw[4] = {qq.x, qq.y, qq.z, qq.w};
-                const uint32_t kw4[4] = {kk.x, kk.y, kk.z, kk.w};
+                if constexpr (PART) {
+                    const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float h0 = lo_f(hw[e]), h1 = hi_f(hw[e]);
-                    const float k0 = lo_f(kyw[e]), k1 = hi_f(kyw[e]);
-                    const float w0 = lo_f(qw[e]) * lo_f(kw4[e]);
-                    const float w1 = hi_f(qw[e]) * hi_f(kw4[e]);
-                    acc[s] += h0 * h0;
-                    acc[s] += h1 * h1;
-                    acc[HC + s] += k0 * k0;
-                    acc[HC + s] += k1 * k1;
-                    const float p0 = (h0 * w0) * k0;
-                    const float p1 = (h1 * w1) * k1;
-                    acc[2 * HC + s] += p0;
-                    acc[2 * HC + s] += p1;
+                    for (int e = 0; e < 4; ++e) {
+                        const float h0 = lo_f(hw[e]), h1 = hi_f(hw[e]);
+                        acc[s] += h0 * h0;
+                        acc[s] += h1 * h1;
+                    }
+                } else {
+                    const uint4 key = *reinterpret_cast<const uint4*>(kvt + (int64_t)s * dim + c * 8);
+                    const uint4 qq = *reinterpret_cast<const uint4*>(q + (int64_t)s * dim + c * 8);
+                    const uint4 kk = *reinterpret_cast<const uint4*>(kw + (int64_t)s * dim + c * 8);
+                    const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
+                    const uint32_t kyw[4] = {key.x, key.y, key.z, key.w};
+                    const uint32_t qw[4] = {qq.x, qq.y, qq.z, qq.w};
+                    const uint32_t kw4[4] = {kk.x, kk.y, kk.z, kk.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float h0 = lo_f(hw[e]), h1 = hi_f(hw[e]);
+                        const float k0 = lo_f(kyw[e]), k1 = hi_f(kyw[e]);
+                        const float w0 = lo_f(qw[e]) * lo_f(kw4[e]);
+                        const float w1 = hi_f(qw[e]) * hi_f(kw4[e]);
+                        acc[s] += h0 * h0;
+                        acc[s] += h1 * h1;
+                        acc[HC + s] += k0 * k0;
+                        acc[HC + s] += k1 * k1;
+                        const float p0 = (h0 * w0) * k0;
+                        const float p1 = (h1 * w1) * k1;
+                        acc[2 * HC + s] += p0;
+                        acc[2 * HC + s] += p1;
+                    }
                 }
             }
         }
@@ -136,8 +161,18 @@ __global__ void __launch_bounds__(1024) gate_kernel(
         float shh = 0.f, skk = 0.f, shwk = 0.f;
         for (int w = 0; w < nwaves; ++w) {
             shh += red[w][tid];
-            skk += red[w][HC + tid];
-            shwk += red[w][2 * HC + tid];
+            if constexpr (!PART) {
+                skk += red[w][HC + tid];
+                shwk += red[w][2 * HC + tid];
+            }
+        }
+        if constexpr (PART) {
+            const int nq = dim >> 7;
+            for (int b = 0; b < nq; ++b) {
+                const float2 p = psh[tid * nq + b];
+                skk += p.x;
+                shwk += p.y;
+            }
         }
         const float fd = (float)dim;
         const float rstd = (1.0f / sqrtf(shh / fd + eps)) * (1.0f / sqrtf(skk / fd + eps));
@@ -158,7 +193,7 @@ __global__ void __launch_bounds__(1024) gate_kernel(
         const int c = tid + i * nthr;
         if (c < d8) {
             const uint4 vv = KEEP ? vr[i < KC ? i : 0]
-                                  : *reinterpret_cast<const uint4*>(kvt + (int64_t)HC * dim + c * 8);
+                                  : *reinterpret_cast<const uint4*>(kvt + voff + c * 8);
             const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
             for (int s = 0; s < HC; ++s) {
@@ -178,10 +213,10 @@ __global__ void __launch_bounds__(1024) gate_kernel(
     }
 }
 
-template <int HC>
+template <int HC, bool PART>
 hipError_t run_hc(const Geom& g, const uint16_t* x, const uint16_t* kv, const uint16_t* q,
-                  const uint16_t* k, const uint8_t* mask, int64_t n_tok, uint16_t* out,
-                  float* gate, hipStream_t s) {
+                  const uint16_t* k, const float2* part, const uint8_t* mask, int64_t n_tok,
+                  uint16_t* out, float* gate, hipStream_t s) {
     const int d8 = g.dim / 8;
     // one 16-byte chunk per thread and stream up to 1024 threads (640 at
     // dim 5120): measured faster than fewer threads holding more chunks
@@ -193,8 +228,8 @@ hipError_t run_hc(const Geom& g, const uint16_t* x, const uint16_t* kv, const ui
     const dim3 grid((unsigned)n_tok), block(threads);
 #define ENGRAM_GATE_CASE(N)                                                                  \
     case N:                                                                                  \
-        gate_kernel<HC, N><<<grid, block, 0, s>>>(x, kv, q, k, mask, g.dim, g.eps,           \
-                                                  inv_sqrt_dim, out, gate);                  \
+        gate_kernel<HC, N, PART><<<grid, block, 0, s>>>(x, kv, q, k, part, mask, g.dim,      \
+                                                        g.eps, inv_sqrt_dim, out, gate);     \
         break;
     switch (nch) {
         ENGRAM_GATE_CASE(1)
@@ -213,14 +248,32 @@ hipError_t launch_gate_add(const Geom& g, const uint16_t* x, const uint16_t* kv,
                            int64_t n_tok, uint16_t* out, float* gate, hipStream_t s) {
     if (n_tok == 0) return hipSuccess;
     switch (g.hc) {
-        case 1: return run_hc<1>(g, x, kv, q, k, mask, n_tok, out, gate, s);
-        case 2: return run_hc<2>(g, x, kv, q, k, mask, n_tok, out, gate, s);
-        case 3: return run_hc<3>(g, x, kv, q, k, mask, n_tok, out, gate, s);
-        case 4: return run_hc<4>(g, x, kv, q, k, mask, n_tok, out, gate, s);
-        case 5: return run_hc<5>(g, x, kv, q, k, mask, n_tok, out, gate, s);
-        case 6: return run_hc<6>(g, x, kv, q, k, mask, n_tok, out, gate, s);
-        case 7: return run_hc<7>(g, x, kv, q, k, mask, n_tok, out, gate, s);
-        case 8: return run_hc<8>(g, x, kv, q, k, mask, n_tok, out, gate, s);
+        case 1: return run_hc<1, false>(g, x, kv, q, k, nullptr, mask, n_tok, out, gate, s);
+        case 2: return run_hc<2, false>(g, x, kv, q, k, nullptr, mask, n_tok, out, gate, s);
+        case 3: return run_hc<3, false>(g, x, kv, q, k, nullptr, mask, n_tok, out, gate, s);
+        case 4: return run_hc<4, false>(g, x, kv, q, k, nullptr, mask, n_tok, out, gate, s);
+        case 5: return run_hc<5, false>(g, x, kv, q, k, nullptr, mask, n_tok, out, gate, s);
+        case 6: return run_hc<6, false>(g, x, kv, q, k, nullptr, mask, n_tok, out, gate, s);
+        case 7: return run_hc<7, false>(g, x, kv, q, k, nullptr, mask, n_tok, out, gate, s);
+        case 8: return run_hc<8, false>(g, x, kv, q, k, nullptr, mask, n_tok, out, gate, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_gate_from_partials(const Geom& g, const uint16_t* x, const uint16_t* v,
+                                     const float2* part, const uint8_t* mask, int64_t n_tok,
+                                     uint16_t* out, float* gate, hipStream_t s) {
+    if (n_tok == 0) return hipSuccess;
+    if (g.dim % 128 != 0) return hipErrorInvalidValue;
+    switch (g.hc) {
+        case 1: return run_hc<1, true>(g, x, v, nullptr, nullptr, part, mask, n_tok, out, gate, s);
+        case 2: return run_hc<2, true>(g, x, v, nullptr, nullptr, part, mask, n_tok, out, gate, s);
+        case 3: return run_hc<3, true>(g, x, v, nullptr, nullptr, part, mask, n_tok, out, gate, s);
+        case 4: return run_hc<4, true>(g, x, v, nullptr, nullptr, part, mask, n_tok, out, gate, s);
+        case 5: return run_hc<5, true>(g, x, v, nullptr, nullptr, part, mask, n_tok, out, gate, s);
+        case 6: return run_hc<6, true>(g, x, v, nullptr, nullptr, part, mask, n_tok, out, gate, s);
+        case 7: return run_hc<7, true>(g, x, v, nullptr, nullptr, part, mask, n_tok, out, gate, s);
+        case 8: return run_hc<8, true>(g, x, v, nullptr, nullptr, part, mask, n_tok, out, gate, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -44,6 +44,20 @@ hipError_t launch_gather(const Geom& g, const uint8_t* table, const uint8_t* sca
 hipError_t launch_wkv(const uint16_t* a, const uint16_t* w, int64_t M, int N, int K,
                       uint16_t* kv, hipStream_t s);
 
+// The gate's key-side reductions done in the projection's epilogue (fully
+// fused prefill): for key columns the projection writes, per (position m,
+// stream s, 128-column block b of the stream), the partial sums over that
+// block of key^2 and (h*w)*key, w = q*k, with the key rounded to bf16 as it
+// would be stored; key columns never reach memory.  The value columns go to
+// C = v [M, dim].
+struct GatePartials {
+    const uint16_t* x;  // [M, hc, dim] bf16
+    const uint16_t* q;  // [hc, dim] bf16
+    const uint16_t* k;  // [hc, dim] bf16
+    float2* part;       // [M, hc, dim / 128] (sum key^2, sum (h*w)*key)
+    int dim, hc;
+};
+
 // number of compute units of the current device (cached)
 int cu_count();
 
@@ -53,6 +67,22 @@ size_t gathered_scratch_bytes(const Geom& g, int64_t M);
 hipError_t launch_wkv_gathered(const Geom& g, const int32_t* hash_ids, const uint8_t* table,
                                const uint8_t* scales, const uint16_t* w, int64_t M, uint16_t* kv,
                                void* scratch, uint32_t* err, hipStream_t s);
+
+// The same projection with the gate's key reductions in its epilogue (see
+// GatePartials); writes v [M, dim] and gp.part.  Only where
+// gate_partials_supported(g, M).
+bool gate_partials_supported(const Geom& g, int64_t M);
+hipError_t launch_wkv_gate_partials(const Geom& g, const int32_t* hash_ids, const uint8_t* table,
+                                    const uint8_t* scales, const uint16_t* w, int64_t M,
+                                    const GatePartials& gp, uint16_t* v, void* scratch,
+                                    uint32_t* err, hipStream_t s);
+
+// Stage 4 from the partial sums: per (token, stream) S_hh from x, S_kk and
+// S_hwk as the fixed-order sum of the dim/128 partials, then g and
+// out = bf16(h + g*v).
+hipError_t launch_gate_from_partials(const Geom& g, const uint16_t* x, const uint16_t* v,
+                                     const float2* part, const uint8_t* mask, int64_t n_tok,
+                                     uint16_t* out, float* gate, hipStream_t s);
 
 hipError_t launch_gate_add(const Geom& g, const uint16_t* x, const uint16_t* kv,
                            const uint16_t* q, const uint16_t* k, const uint8_t* mask,

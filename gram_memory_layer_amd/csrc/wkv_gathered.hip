@@ -108,6 +108,9 @@ using IC = std::integral_constant<int, V>;
 //     point, so neither the start-up latency of a tile nor its stores stall
 //     the matrix pipe for long.  The last tile loads its own first k-tiles a
 //     second time (harmless; they land before the workgroup ends).
+//   gp.x != nullptr (persistent only): tiles of key columns (n0 < hc*dim)
+//     end in the gate's partial sums instead of a store; value columns go to
+//     C at column n - hc*dim.
 template <int BT, int WMV, int WNV, int L, bool P>
 __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
                                               const float2* __restrict__ scl, int n_cols,
@@ -115,7 +118,7 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
                                               int64_t num_rows, const uint16_t* __restrict__ W,
                                               int64_t M, int N, uint16_t* __restrict__ C,
                                               int64_t ldc, int tiles_m, int tiles_n, int per_xcd,
-                                              uint8_t* smem) {
+                                              const GatePartials& gp, uint8_t* smem) {
     constexpr int NW = WMV * WNV;
     constexpr int WM = BT / WMV, WN = BT / WNV;
     constexpr int TI = WM / 32, TJ = WN / 32;
@@ -398,7 +401,60 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
             return gq < BT / 16 ? (uint32_t)((gq * G_NS + 2) * 1024)
                                 : (uint32_t)(OFF_W + ((gq - BT / 16) * G_NS + 2) * 1024);
         };
+        const int kcols = gp.x ? gp.hc * gp.dim : 0;  // key columns: reduced, not stored
+        // Key tile: per row, the sums over this wave's 128 columns of key^2
+        // and (h*w)*key, the key rounded to bf16 first; products are rounded
+        // before they are added (no fused multiply-add), each lane sums its
+        // 64 values in a fixed order and adds the other lane half's.
+        auto gate_partials = [&]() {
+#pragma clang fp contract(off)
+            const int s = n0c / gp.dim, f0 = n0c - s * gp.dim + wn * WN;
+            const int nq = gp.dim >> 7;
+            const __amdgpu_buffer_rsrc_t rx =
+                make_rsrc(gp.x, (uint32_t)(M * gp.hc * gp.dim * 2));  // rows past M read 0
+            const __amdgpu_buffer_rsrc_t rq = make_rsrc(gp.q, (uint32_t)(gp.hc * gp.dim * 2));
+            const __amdgpu_buffer_rsrc_t rk = make_rsrc(gp.k, (uint32_t)(gp.hc * gp.dim * 2));
+            const uint32_t qk0 = (uint32_t)((s * gp.dim + f0) * 2);
+#pragma unroll
+            for (int i = 0; i < TI; ++i) {
+                const int64_t m = (int64_t)m0c + wm * WM + i * 32 + lrow;
+                const uint32_t xr = (uint32_t)(((m * gp.hc + s) * gp.dim + f0) * 2);
+                float skk = 0.0f, shwk = 0.0f;
+#pragma unroll
+                for (int j = 0; j < TJ; ++j)
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const uint32_t nl = (uint32_t)(j * 32 + 8 * g4 + 4 * lhalf) * 2;
+                        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                        const u32x2 hx = __builtin_amdgcn_raw_buffer_load_b64(rx, xr + nl, 0, 0);
+                        const u32x2 qq = __builtin_amdgcn_raw_buffer_load_b64(rq, qk0 + nl, 0, 0);
+                        const u32x2 kk = __builtin_amdgcn_raw_buffer_load_b64(rk, qk0 + nl, 0, 0);
+                        const uint32_t kb[2] = {
+                            pack_bf16(acc[j][i][4 * g4 + 0], acc[j][i][4 * g4 + 1]),
+                            pack_bf16(acc[j][i][4 * g4 + 2], acc[j][i][4 * g4 + 3])};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int sh = (e & 1) ? 0 : 16;  // low half first
+                            const uint32_t hb = hx[e >> 1], qb = qq[e >> 1], kw = kk[e >> 1];
+                            const float key = __uint_as_float((kb[e >> 1] << sh) & 0xFFFF0000u);
+                            const float h = __uint_as_float((hb << sh) & 0xFFFF0000u);
+                            const float w = __uint_as_float((qb << sh) & 0xFFFF0000u) *
+                                            __uint_as_float((kw << sh) & 0xFFFF0000u);
+                            skk += key * key;
+                            shwk += (h * w) * key;
+                        }
+                    }
+                skk += __shfl_xor(skk, 32, 64);
+                shwk += __shfl_xor(shwk, 32, 64);
+                if (lhalf == 0 && m < M)
+                    gp.part[(m * gp.hc + s) * nq + (f0 >> 7)] = make_float2(skk, shwk);
+            }
+        };
         auto epilogue = [&]() {
+            if (gp.x && n0c < kcols) {
+                gate_partials();
+                return;
+            }
 #pragma unroll
             for (int f0 = 0; f0 < NF; f0 += FP) {
 #pragma unroll
@@ -425,7 +481,7 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
                             smem + blk(2 * s + hh) + (rr & 15) * 64 + sl * 16);
                         const int64_t m = (int64_t)m0c + wm * WM + i * 32 + rr;
                         const int n = n0c + wn * WN + j * 32 + ((sl ^ (rr & 3)) << 3);
-                        if (m < M && n < N) *reinterpret_cast<uint4*>(C + m * ldc + n) = v;
+                        if (m < M && n < N) *reinterpret_cast<uint4*>(C + m * ldc + (n - kcols)) = v;
                     }
                 }
             }
@@ -515,10 +571,10 @@ __global__ void __launch_bounds__(512, 1)
 wkv_gathered_256(const uint32_t* __restrict__ aoff, const float2* __restrict__ scl, int n_cols,
                  int64_t m_pad, const uint8_t* __restrict__ table, int64_t num_rows,
                  const uint16_t* __restrict__ W, int64_t M, int N, uint16_t* __restrict__ C,
-                 int64_t ldc, int tiles_m, int tiles_n, int per_xcd) {
+                 int64_t ldc, int tiles_m, int tiles_n, int per_xcd, GatePartials gp) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM256];
     gathered_tile<256, 4, 2, L, P>(aoff, scl, n_cols, m_pad, table, num_rows, W, M, N, C, ldc,
-                                   tiles_m, tiles_n, per_xcd, smem);
+                                   tiles_m, tiles_n, per_xcd, gp, smem);
 }
 
 template <int L>
@@ -528,8 +584,9 @@ wkv_gathered_128(const uint32_t* __restrict__ aoff, const float2* __restrict__ s
                  const uint16_t* __restrict__ W, int64_t M, int N, uint16_t* __restrict__ C,
                  int64_t ldc, int tiles_m, int tiles_n, int per_xcd) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM128];
+    const GatePartials none{};
     gathered_tile<128, 2, 2, L, false>(aoff, scl, n_cols, m_pad, table, num_rows, W, M, N, C, ldc,
-                                       tiles_m, tiles_n, per_xcd, smem);
+                                       tiles_m, tiles_n, per_xcd, none, smem);
 }
 
 template <int L>
@@ -543,7 +600,8 @@ hipError_t run_gathered_l(int bt, const uint32_t* aoff, const float2* scl, int n
     const int per_xcd = (total + N_XCD - 1) / N_XCD;
     if (bt == 256)
         wkv_gathered_256<L, false><<<dim3(per_xcd * N_XCD), dim3(512), 0, s>>>(
-            aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, tiles_m, tiles_n, per_xcd);
+            aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, tiles_m, tiles_n, per_xcd,
+            GatePartials{});
     else
         wkv_gathered_128<L><<<dim3(per_xcd * N_XCD), dim3(256), 0, s>>>(
             aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, tiles_m, tiles_n, per_xcd);
@@ -568,7 +626,8 @@ hipError_t run_gathered(int bt, const uint32_t* aoff, const float2* scl, int n_c
 // slot, slot + nwg, ...  Needs nk % 3 == 0 and N a multiple of 256.
 hipError_t run_persistent(const uint32_t* aoff, const float2* scl, int n_cols, int64_t m_pad,
                           const uint8_t* table, int64_t num_rows, const uint16_t* w, int64_t M,
-                          int N, uint16_t* c, int64_t ldc, int cus, hipStream_t s) {
+                          int N, uint16_t* c, int64_t ldc, int cus, const GatePartials& gp,
+                          hipStream_t s) {
     const int tiles_m = (int)((M + 255) / 256);
     const int tiles_n = N / 256;
     const int total = tiles_m * tiles_n;
@@ -576,11 +635,44 @@ hipError_t run_persistent(const uint32_t* aoff, const float2* scl, int n_cols, i
     int grid = cus / N_XCD * N_XCD;
     if (grid > per_xcd * N_XCD) grid = per_xcd * N_XCD;
     wkv_gathered_256<3, true><<<dim3(grid), dim3(512), 0, s>>>(
-        aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, tiles_m, tiles_n, per_xcd);
+        aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, tiles_m, tiles_n, per_xcd, gp);
     return hipGetLastError();
 }
 
 int64_t padded_rows(int64_t M) { return (M + 255) / 256 * 256; }
+
+hipError_t launch_prep(const Geom& g, const int32_t* hash_ids, const uint8_t* scales, int64_t M,
+                       int64_t m_pad, uint32_t* aoff, float2* scl, uint32_t* err, hipStream_t s) {
+    const int64_t total = (int64_t)g.n_cols * m_pad;
+    prep_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s>>>(
+        hash_ids, g.n_cols, M, m_pad, scales, g.num_embeddings, aoff, scl, err);
+    return hipGetLastError();
+}
+
+// Columns [0, nbig) run in 256x256 tiles, the rest in 128x128 tiles: nbig is
+// the widest multiple of 256 whose tile count fills whole rounds of the
+// machine, provided the 128x128 rest fits in one round (else all of N).
+int big_columns(int64_t M, int N, int cus) {
+    const int tiles_m = (int)((M + 255) / 256);
+    const int tiles_n = (N + 255) / 256;
+    int nb = tiles_n;
+    if ((int64_t)tiles_m * tiles_n % cus != 0) {
+        int cand = tiles_n - 1;
+        while (cand > 0 && (int64_t)tiles_m * cand % cus != 0) --cand;
+        if (cand > 0) {
+            const int64_t small = ((M + 127) / 128) * ((N - cand * 256 + 127) / 128);
+            if (small <= cus) nb = cand;
+        }
+    }
+    return nb * 256 < N ? nb * 256 : N;
+}
+
+// the persistent kernel: nk a multiple of 3, whole 256-column tiles, and at
+// least two tiles per compute unit
+bool persistent_ok(const Geom& g, int64_t M, int nbig, int cus) {
+    return g.n_cols % 3 == 0 && nbig % 256 == 0 && cus >= N_XCD &&
+           ((M + 255) / 256) * (nbig / 256) >= 2 * (int64_t)cus;
+}
 
 }  // namespace
 
@@ -608,37 +700,53 @@ hipError_t launch_wkv_gathered(const Geom& g, const int32_t* hash_ids, const uin
     uint32_t* aoff = reinterpret_cast<uint32_t*>(scratch);
     float2* scl = reinterpret_cast<float2*>(aoff + (int64_t)g.n_cols * m_pad);
     {
-        const int64_t total = (int64_t)g.n_cols * m_pad;
-        prep_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s>>>(
-            hash_ids, g.n_cols, M, m_pad, scales, g.num_embeddings, aoff, scl, err);
-        hipError_t e = hipGetLastError();
+        hipError_t e = launch_prep(g, hash_ids, scales, M, m_pad, aoff, scl, err, s);
         if (e != hipSuccess) return e;
     }
     const int N = g.N;
     const int cus = cu_count();
-    const int tiles_m = (int)((M + 255) / 256);
-    const int tiles_n = (N + 255) / 256;
-    int nb = tiles_n;
-    if ((int64_t)tiles_m * tiles_n % cus != 0) {
-        int cand = tiles_n - 1;
-        while (cand > 0 && (int64_t)tiles_m * cand % cus != 0) --cand;
-        if (cand > 0) {
-            const int64_t small = ((M + 127) / 128) * ((N - cand * 256 + 127) / 128);
-            if (small <= cus) nb = cand;
-        }
-    }
-    const int nbig = nb * 256 < N ? nb * 256 : N;
+    const int nbig = big_columns(M, N, cus);
     hipError_t e;
-    if (g.n_cols % 3 == 0 && nbig % 256 == 0 && cus >= N_XCD &&
-        (int64_t)tiles_m * (nbig / 256) >= 2 * cus)
+    if (persistent_ok(g, M, nbig, cus))
         e = run_persistent(aoff, scl, g.n_cols, m_pad, table, g.num_embeddings, w, M, nbig, kv, N,
-                           cus, s);
+                           cus, GatePartials{}, s);
     else
         e = run_gathered(256, aoff, scl, g.n_cols, m_pad, table, g.num_embeddings, w, M, nbig, kv,
                          N, s);
     if (e != hipSuccess || nbig >= N) return e;
     return run_gathered(128, aoff, scl, g.n_cols, m_pad, table, g.num_embeddings,
                         w + (int64_t)nbig * g.K, M, N - nbig, kv + nbig, N, s);
+}
+
+bool gate_partials_supported(const Geom& g, int64_t M) {
+    if (!gathered_supported(g, M) || g.dim % 256 != 0) return false;
+    if (M * g.hc * g.dim * 2 >= ((int64_t)1 << 32)) return false;  // x under one descriptor
+    const int cus = cu_count();
+    const int nbig = big_columns(M, g.N, cus);
+    return nbig >= g.hc * g.dim && persistent_ok(g, M, nbig, cus);
+}
+
+// The persistent 256x256 kernel covers every key column (and the first value
+// columns); the 128x128 tail, if any, holds value columns only.
+hipError_t launch_wkv_gate_partials(const Geom& g, const int32_t* hash_ids, const uint8_t* table,
+                                    const uint8_t* scales, const uint16_t* w, int64_t M,
+                                    const GatePartials& gp, uint16_t* v, void* scratch,
+                                    uint32_t* err, hipStream_t s) {
+    if (M == 0) return hipSuccess;
+    if (!gate_partials_supported(g, M) || gp.dim != g.dim || gp.hc != g.hc) return hipErrorInvalidValue;
+    const int64_t m_pad = padded_rows(M);
+    uint32_t* aoff = reinterpret_cast<uint32_t*>(scratch);
+    float2* scl = reinterpret_cast<float2*>(aoff + (int64_t)g.n_cols * m_pad);
+    hipError_t e = launch_prep(g, hash_ids, scales, M, m_pad, aoff, scl, err, s);
+    if (e != hipSuccess) return e;
+    const int cus = cu_count();
+    const int nbig = big_columns(M, g.N, cus);
+    const int kcols = g.hc * g.dim;
+    e = run_persistent(aoff, scl, g.n_cols, m_pad, table, g.num_embeddings, w, M, nbig, v, g.dim,
+                       cus, gp, s);
+    if (e != hipSuccess || nbig >= g.N) return e;
+    return run_gathered(128, aoff, scl, g.n_cols, m_pad, table, g.num_embeddings,
+                        w + (int64_t)nbig * g.K, M, g.N - nbig, v + (nbig - kcols), g.dim, s);
 }
 
 }  // namespace engram

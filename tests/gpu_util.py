@@ -40,8 +40,9 @@ class Workload:
     """Every given input of one configuration, on the device (bulk tensors
     drawn there) and the host tables."""
 
-    def __init__(self, ge, name: str, dev, with_table: bool = True, with_weights: bool = True):
-        self.cfg = cfg = synth.config(name)
+    def __init__(self, ge, name, dev, with_table: bool = True, with_weights: bool = True):
+        """`name`: a configuration name, or a synth.Config itself."""
+        self.cfg = cfg = synth.config(name) if isinstance(name, str) else name
         self.t = synth.hash_tables(cfg)
         self.num_emb = self.t["num_embeddings"]
         self.g = geometry(ge, cfg, self.num_emb)

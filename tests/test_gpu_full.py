@@ -113,6 +113,42 @@ def test_prefill_full(ge, dev):
     say("   gate", gs, "out", os_)
 
 
+# ------------------------------------------------------------------ fully fused prefill
+@pytest.mark.parametrize("dim,n_heads,T,inplace", [(2048, 3, 4096, False), (2048, 3, 4000, True)])
+def test_forward_gate_partials_geometry(ge, dev, dim, n_heads, T, inplace):
+    # a smaller geometry that still takes the fully fused path (gate sums in
+    # the projection's epilogue): dim 2048, 6 hash columns, masked positions,
+    # a ragged last 256-row tile when T = 4000, out written over x
+    import dataclasses
+    cfg = dataclasses.replace(synth.config("prefill"), dim=dim, n_heads=n_heads, T=T,
+                              mask_frac=0.2)
+    say("fused-gate forward", dim, n_heads, T, "in place" if inplace else "")
+    wl = Workload(ge, cfg, dev)
+    ids_np = synth.token_ids(cfg, 1, T)
+    ids = torch.from_numpy(ids_np).to(dev)
+    x = synth.activations(cfg, T, dev).reshape(1, T, cfg.hc_mult, cfg.dim)
+    mask_np = synth.token_mask(cfg, 1, T)
+    mask = torch.from_numpy(mask_np).to(dev)
+    xb = bits(x).reshape(T, cfg.hc_mult, cfg.dim)
+    gate = torch.empty((1, T, cfg.hc_mult), dtype=torch.float32, device=dev)
+    layer = ge.EngramLayer(wl.g, wl.tables, wl.table, wl.scales, wl.w, wl.q, wl.k)
+    out = layer.forward(x, ids, mask=mask, gate=gate, out=x if inplace else None)
+    torch.cuda.synchronize()
+    pos = _sample_positions(T, extra=(255, 256, T - 257, T - 256), n=10, seed=T)
+    mk = mask_np.reshape(-1)
+    ref = _oracle_tokens(wl, ids_np[0], pos, xb[pos], mk[pos])
+    ref["_q"], ref["_k"] = bits(wl.q), bits(wl.k)
+    gs, os_ = _check_tokens(ref, bits(out).reshape(T, cfg.hc_mult, cfg.dim)[pos],
+                            gate.cpu().numpy().reshape(T, -1)[pos], xb[pos], cfg)
+    say("   gate", gs, "out", os_)
+    # masked positions pass x through bit for bit, with gate 0
+    masked = np.nonzero(mk == 0)[0][:50]
+    if len(masked):
+        ob = bits(out).reshape(T, cfg.hc_mult, cfg.dim)[masked]
+        assert np.array_equal(ob, xb[masked])
+        assert np.all(gate.cpu().numpy().reshape(T, -1)[masked] == 0)
+
+
 # ------------------------------------------------------------------ projection tiling
 @pytest.mark.parametrize("M", [2048, 4096])
 def test_wkv_full_width_tail_split(ge, dev, M):
