@@ -10,6 +10,7 @@ library is not built, every call raises.
 Functions carry the C names:
     engram_hash, engram_gather, engram_wkv, engram_wkv_gathered, engram_gate_add,
     engram_forward, engram_forward_workspace_size, engram_wkv_gathered_scratch_size,
+    engram_gate_partials_supported, engram_wkv_gate_partials, engram_gate_from_partials,
     engram_check_geometry
 plus ``Geometry`` / ``HashTables`` (the C structs) and ``EngramLayer``, a
 holder for one layer's device tables, weights and workspace.
@@ -25,6 +26,7 @@ __all__ = [
     "Geometry", "HashTables", "EngramError", "EngramLayer", "load", "library_path",
     "engram_check_geometry", "engram_hash", "engram_gather", "engram_wkv",
     "engram_wkv_gathered", "engram_wkv_gathered_scratch_size",
+    "engram_gate_partials_supported", "engram_wkv_gate_partials", "engram_gate_from_partials",
     "engram_gate_add", "engram_forward", "engram_forward_workspace_size",
     "ERRBIT_TOKEN", "ERRBIT_HASH", "ERRBIT_ROW",
 ]
@@ -104,6 +106,12 @@ def load():
     L.engram_wkv_gathered_scratch_size.argtypes = [G, i64]
     L.engram_wkv_gathered.restype = C.c_int
     L.engram_wkv_gathered.argtypes = [G, P, P, P, i64, P, P, P, C.c_size_t, P, P]
+    L.engram_gate_partials_supported.restype = C.c_int
+    L.engram_gate_partials_supported.argtypes = [G, i64]
+    L.engram_wkv_gate_partials.restype = C.c_int
+    L.engram_wkv_gate_partials.argtypes = [G, P, P, P, i64, P, P, P, P, P, P, P, C.c_size_t, P, P]
+    L.engram_gate_from_partials.restype = C.c_int
+    L.engram_gate_from_partials.argtypes = [G, P, P, P, P, i64, P, P, P]
     L.engram_gate_add.restype = C.c_int
     L.engram_gate_add.argtypes = [G, P, P, P, P, P, i64, P, P, P]
     L.engram_forward_workspace_size.restype = C.c_size_t
@@ -251,6 +259,71 @@ def engram_wkv_gathered(g: Geometry, table, scales, hash_ids, w, kv=None, scratc
         C.byref(g), table.data_ptr(), scales.data_ptr(), hid.data_ptr(), M, w.data_ptr(),
         kv.data_ptr(), scratch.data_ptr(), scratch.numel(), _ptr(err), _stream(dev)))
     return kv
+
+
+def engram_gate_partials_supported(g: Geometry, M: int) -> bool:
+    return bool(load().engram_gate_partials_supported(C.byref(g), int(M)))
+
+
+def engram_wkv_gate_partials(g: Geometry, table, scales, hash_ids, w, x, q, k, v=None, part=None,
+                             scratch=None, err=None):
+    """Fused gather + projection whose key columns become the gate's partial
+    sums: returns (v bf16 [n_tok, dim], part fp32 [n_tok, hc, dim/128, 2])."""
+    L = load()
+    dev = hash_ids.device
+    _dev(table, "table", torch.uint8, (g.num_embeddings, g.head_dim), dev)
+    _dev(scales, "scales", torch.uint8, (g.num_embeddings, g.head_dim // 32), dev)
+    _dev(hash_ids, "hash_ids", torch.int32, None, dev)
+    hid = hash_ids.reshape(-1, g.n_hash_cols)
+    M = hid.shape[0]
+    _dev(w, "w", torch.bfloat16, (g.N, g.K), dev)
+    _dev(x, "x", torch.bfloat16, None, dev)
+    if x.numel() != M * g.hc_mult * g.dim:
+        raise ValueError("x must hold n_tok*hc_mult*dim values")
+    _dev(q, "q", torch.bfloat16, (g.hc_mult, g.dim), dev)
+    _dev(k, "k", torch.bfloat16, (g.hc_mult, g.dim), dev)
+    if v is None:
+        v = torch.empty((M, g.dim), dtype=torch.bfloat16, device=dev)
+    _dev(v, "v", torch.bfloat16, (M, g.dim), dev)
+    if part is None:
+        part = torch.empty((M, g.hc_mult, g.dim // 128, 2), dtype=torch.float32, device=dev)
+    _dev(part, "part", torch.float32, (M, g.hc_mult, g.dim // 128, 2), dev)
+    need = engram_wkv_gathered_scratch_size(g, M)
+    if scratch is None:
+        scratch = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev(scratch, "scratch", torch.uint8, None, dev)
+    if err is not None:
+        _dev(err, "err", torch.int32, (1,), dev)
+    _check("engram_wkv_gate_partials", L.engram_wkv_gate_partials(
+        C.byref(g), table.data_ptr(), scales.data_ptr(), hid.data_ptr(), M, w.data_ptr(),
+        x.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(), part.data_ptr(),
+        scratch.data_ptr(), scratch.numel(), _ptr(err), _stream(dev)))
+    return v, part
+
+
+def engram_gate_from_partials(g: Geometry, x, v, part, mask=None, out=None, gate=None):
+    """x bf16 [n_tok, hc, dim] (any leading shape), v bf16 [n_tok, dim], part from
+    engram_wkv_gate_partials -> out (like x); `out` may be x."""
+    L = load()
+    dev = x.device
+    _dev(x, "x", torch.bfloat16, None, dev)
+    n_tok = x.numel() // (g.hc_mult * g.dim)
+    if x.numel() != n_tok * g.hc_mult * g.dim or x.shape[-1] != g.dim:
+        raise ValueError("x must be [..., hc_mult, dim]")
+    _dev(v, "v", torch.bfloat16, (n_tok, g.dim), dev)
+    _dev(part, "part", torch.float32, (n_tok, g.hc_mult, g.dim // 128, 2), dev)
+    m = _mask(mask, n_tok, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _dev(out, "out", torch.bfloat16, tuple(x.shape), dev)
+    if gate is not None:
+        _dev(gate, "gate", torch.float32, None, dev)
+        if gate.numel() != n_tok * g.hc_mult:
+            raise ValueError("gate must hold n_tok*hc_mult values")
+    _check("engram_gate_from_partials", L.engram_gate_from_partials(
+        C.byref(g), x.data_ptr(), v.data_ptr(), part.data_ptr(), _ptr(m), n_tok, out.data_ptr(),
+        _ptr(gate), _stream(dev)))
+    return out
 
 
 def engram_gate_add(g: Geometry, x, kv, q, k, mask=None, out=None, gate=None):

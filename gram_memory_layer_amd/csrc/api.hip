@@ -150,6 +150,54 @@ engram_status engram_gate_add(const engram_geometry* g, const uint16_t* x, const
                                             (hipStream_t)stream));
 }
 
+int engram_gate_partials_supported(const engram_geometry* g, int64_t M) {
+    if (engram_check_geometry(g) != ENGRAM_OK || M < 1 || M >= kMaxTokens) return 0;
+    return engram::gate_partials_supported(engram::make_geom(*g), M) ? 1 : 0;
+}
+
+engram_status engram_wkv_gate_partials(const engram_geometry* g, const uint8_t* table,
+                                       const uint8_t* scales, const int32_t* hash_ids,
+                                       int64_t M, const uint16_t* w, const uint16_t* x,
+                                       const uint16_t* q, const uint16_t* k, uint16_t* v,
+                                       float* part, void* scratch, size_t scratch_bytes,
+                                       uint32_t* err, void* stream) {
+    engram_status st = engram_check_geometry(g);
+    if (st != ENGRAM_OK) return st;
+    if (M < 0 || M >= kMaxTokens) return ENGRAM_ERR_INVALID_ARG;
+    if (M == 0) return ENGRAM_OK;
+    const Geom gg = engram::make_geom(*g);
+    if (!engram::gate_partials_supported(gg, M)) return ENGRAM_ERR_UNSUPPORTED;
+    if (!table || !scales || !hash_ids || !w || !x || !q || !k || !v || !part)
+        return ENGRAM_ERR_INVALID_ARG;
+    if (!aligned16(table) || !aligned16(w) || !aligned16(x) || !aligned16(q) || !aligned16(k) ||
+        !aligned16(v) || ((uintptr_t)part & 7u) != 0 || ((uintptr_t)hash_ids & 3u) != 0)
+        return ENGRAM_ERR_INVALID_ARG;
+    if (scratch == nullptr || scratch_bytes < engram::gathered_scratch_bytes(gg, M) ||
+        ((uintptr_t)scratch & 255u) != 0)
+        return ENGRAM_ERR_WORKSPACE;
+    const engram::GatePartials gp{x, q, k, reinterpret_cast<float2*>(part), gg.dim, gg.hc};
+    return from_hip(engram::launch_wkv_gate_partials(gg, hash_ids, table, scales, w, M, gp, v,
+                                                     scratch, err, (hipStream_t)stream));
+}
+
+engram_status engram_gate_from_partials(const engram_geometry* g, const uint16_t* x,
+                                        const uint16_t* v, const float* part,
+                                        const uint8_t* mask, int64_t n_tok, uint16_t* out,
+                                        float* gate, void* stream) {
+    engram_status st = engram_check_geometry(g);
+    if (st != ENGRAM_OK) return st;
+    if (n_tok < 0 || n_tok >= kMaxTokens) return ENGRAM_ERR_INVALID_ARG;
+    if (g->dim % 128 != 0) return ENGRAM_ERR_UNSUPPORTED;
+    if (n_tok == 0) return ENGRAM_OK;
+    if (!x || !v || !part || !out) return ENGRAM_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(v) || !aligned16(out) || ((uintptr_t)part & 7u) != 0)
+        return ENGRAM_ERR_INVALID_ARG;
+    const Geom gg = engram::make_geom(*g);
+    return from_hip(engram::launch_gate_from_partials(gg, x, v,
+                                                      reinterpret_cast<const float2*>(part), mask,
+                                                      n_tok, out, gate, (hipStream_t)stream));
+}
+
 size_t engram_forward_workspace_size(const engram_geometry* g, int64_t n_tok) {
     if (engram_check_geometry(g) != ENGRAM_OK || n_tok < 0) return 0;
     const Geom gg = engram::make_geom(*g);

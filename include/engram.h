@@ -159,6 +159,36 @@ engram_status engram_gate_add(const engram_geometry* g, const uint16_t* x, const
                               const uint16_t* q, const uint16_t* k, const uint8_t* mask,
                               int64_t n_tok, uint16_t* out, float* gate, void* stream);
 
+/* Fully fused prefill, stages 2-3 ([docs] stages 2-4; [block] forward; [gate]
+ * equation for a_k): engram_wkv_gathered whose key columns are not stored but
+ * reduced, per position m, stream s and 128-column block b of the stream, to
+ *   part[m][s][b] = ( sum key^2, sum (h*w)*key ),  w = q*k,
+ * over the block's columns, with key the bf16 value engram_wkv_gathered would
+ * store and h = x[m][s]; fp32, products rounded before they are added.  The
+ * value columns go to v.
+ *   x bf16 [M, hc_mult, dim]; q, k bf16 [hc_mult, dim];
+ *   v bf16 [M, dim] out;  part float2 [M, hc_mult, dim/128] out (8-byte aligned);
+ *   scratch as in engram_wkv_gathered.
+ * Supported for prefill-sized batches only: head_dim 64, dim % 256 == 0,
+ * n_hash_cols % 3 == 0, at least two 256x256 key/value tiles per compute
+ * unit, M*hc_mult*dim*2 < 2^32; otherwise ENGRAM_ERR_UNSUPPORTED
+ * (engram_gate_partials_supported says which). */
+int engram_gate_partials_supported(const engram_geometry* g, int64_t M);
+engram_status engram_wkv_gate_partials(const engram_geometry* g, const uint8_t* table,
+                                       const uint8_t* scales, const int32_t* hash_ids,
+                                       int64_t M, const uint16_t* w, const uint16_t* x,
+                                       const uint16_t* q, const uint16_t* k, uint16_t* v,
+                                       float* part, void* scratch, size_t scratch_bytes,
+                                       uint32_t* err, void* stream);
+
+/* Stage 4 from the partial sums of engram_wkv_gate_partials: S_hh from x, S_kk
+ * and S_hwk as the in-order sum over b of part[m][s][b], then a, g and out as
+ * in engram_gate_add.  v bf16 [n_tok, dim]; other arguments as there. */
+engram_status engram_gate_from_partials(const engram_geometry* g, const uint16_t* x,
+                                        const uint16_t* v, const float* part,
+                                        const uint8_t* mask, int64_t n_tok, uint16_t* out,
+                                        float* gate, void* stream);
+
 /* Bytes of workspace engram_forward needs for n_tok = B*T positions
  * (hash ids, gathered rows or the fused projection's scratch, and kv). */
 size_t engram_forward_workspace_size(const engram_geometry* g, int64_t n_tok);

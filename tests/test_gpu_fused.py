@@ -172,3 +172,68 @@ def test_fused_full_size(ge, dev, prefill, M):
     st = _check_against_oracle_and_two_stage(ge, wl.g, wl.cfg, wl.table, wl.scales, hid, wl.w,
                                              sample=pos)
     say("   kv", st)
+
+
+# ------------------------------------------------------------------ fully fused prefill
+@pytest.fixture(scope="module")
+def gp_case(ge, dev):
+    # dim 2048, hc 4, 6 hash columns, M = 4096: 640 tiles of 256x256, the
+    # persistent kernel with every key column reduced in its epilogue
+    cfg, rows = _small(2048, 4, 3, 3, rows=200000)
+    g = geometry(ge, cfg, rows)
+    M = 4096
+    assert ge.engram_gate_partials_supported(g, M)
+    table, scales = synth.embedding_table(cfg, rows, dev)
+    w = synth.wkv_weight(cfg, dev)
+    q, k = synth.qk_weights(cfg, dev)
+    x = synth.activations(cfg, M, dev).reshape(M, cfg.hc_mult, cfg.dim)
+    rng = np.random.default_rng(77)
+    hid = torch.from_numpy(rng.integers(0, rows, (M, g.n_hash_cols)).astype(np.int32)).to(dev)
+    kv = ge.engram_wkv_gathered(g, table, scales, hid, w)
+    v, part = ge.engram_wkv_gate_partials(g, table, scales, hid, w, x, q, k)
+    torch.cuda.synchronize()
+    return dict(cfg=cfg, g=g, M=M, q=q, k=k, x=x, kv=kv, v=v, part=part)
+
+
+def test_gate_partials_value_and_sums(ge, dev, gp_case):
+    c = gp_case
+    g, M, cfg = c["g"], c["M"], c["cfg"]
+    hd = cfg.hc_mult * cfg.dim
+    say("gate partials: value columns bit for bit")
+    assert torch.equal(c["v"].view(torch.int16), c["kv"][:, hd:].contiguous().view(torch.int16))
+    say("gate partials: sums against fp64 over the stored keys")
+    rows = np.unique(np.concatenate([[0, 255, 256, M - 1], np.random.default_rng(3).integers(0, M, 28)]))
+    key = tolerances.bf16_value(bits(c["kv"][torch.from_numpy(rows).to(dev)][:, :hd]))
+    key = key.reshape(len(rows), cfg.hc_mult, cfg.dim // 128, 128)
+    h = tolerances.bf16_value(bits(c["x"][torch.from_numpy(rows).to(dev)]))
+    h = h.reshape(key.shape)
+    wq = (tolerances.bf16_value(bits(c["q"])) * tolerances.bf16_value(bits(c["k"])))
+    wq = wq.reshape(1, cfg.hc_mult, cfg.dim // 128, 128)
+    t_kk = key * key
+    t_hwk = (h * wq) * key
+    ref = np.stack([t_kk.sum(-1), t_hwk.sum(-1)], -1)
+    bound = 128 * 2.0 ** -23 * np.stack([np.abs(t_kk).sum(-1), np.abs(t_hwk).sum(-1)], -1) + 1e-30
+    got = c["part"][torch.from_numpy(rows).to(dev)].cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref)
+    assert np.all(err <= bound), "partial sums off by %r of the bound" % float((err / bound).max())
+
+
+def test_gate_from_partials_against_oracle(ge, dev, gp_case):
+    # the gate from the partial sums against the oracle's gate_and_add on the
+    # same kv (the GPU's), with a mask
+    c = gp_case
+    g, M, cfg = c["g"], c["M"], c["cfg"]
+    mask = torch.from_numpy((np.random.default_rng(9).random(M) > 0.25).astype(np.uint8)).to(dev)
+    gate = torch.empty((M, cfg.hc_mult), dtype=torch.float32, device=dev)
+    out = ge.engram_gate_from_partials(g, c["x"], c["v"], c["part"], mask=mask, gate=gate)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, M - 1], np.random.default_rng(4).integers(0, M, 40)]))
+    ri = torch.from_numpy(rows).to(dev)
+    xb, kvb = bits(c["x"][ri]), bits(c["kv"][ri])
+    mk = mask.cpu().numpy()[rows]
+    ref_out, ref_gate, ref_a = oracle.gate_and_add(xb, kvb, bits(c["q"]), bits(c["k"]),
+                                                   cfg.norm_eps, mk)
+    gs = tolerances.check_gate(gate.cpu().numpy()[rows], ref_gate, ref_a)
+    os_ = tolerances.check_out(bits(out[ri]), ref_out, xb, kvb[:, cfg.hc_mult * cfg.dim:],
+                               gate.cpu().numpy()[rows], ref_gate)
+    say("   gate", gs, "out", os_)
