@@ -2,15 +2,17 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
-One step = one engram_forward (hash -> fp8 row gather fused into the wkv
-bf16 MFMA projection -> gate and add) over the DeepSeek-V4.1-shaped prefill:
-B=1, T=4096, dim=5120, hc=4, 24 hash columns of head_dim 64 (wkv 1536 ->
-25600), a 25,160,950-row fp8 table, seeded synthetic inputs already resident
-in HBM.  Prints one JSON line: whole-job tokens/s, the roofline of the
-dominant call, engram_wkv_gathered (projection flops per call over its
-average call time, measured here with HIP events on the stream it runs on;
-the call is the offset/scale prep kernel plus the two projection kernels)
-and the CPU oracle timed on a bounded sample.
+One step = one engram_forward over the DeepSeek-V4.1-shaped prefill: B=1,
+T=4096, dim=5120, hc=4, 24 hash columns of head_dim 64 (wkv 1536 -> 25600),
+a 25,160,950-row fp8 table, seeded synthetic inputs already resident in HBM.
+The forward runs fully fused: hash -> the fp8 row gather fused into the wkv
+bf16 MFMA projection, whose epilogue reduces the key columns into the gate's
+partial sums (engram_wkv_gate_partials) -> the gate from those partials.
+Prints one JSON line: whole-job tokens/s, the roofline of the dominant call,
+engram_wkv_gate_partials (projection flops per call over its average call
+time, measured here with HIP events on the stream it runs on; the call is
+the offset/scale prep kernel plus the two projection kernels), the gate's
+HBM rate, and the CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -28,7 +30,7 @@ if ROOT not in sys.path:
 METRIC = "Engram prefill tokens/s @dim5120 hc4 (1 GPU); % MFMA peak (wkv), % HBM BW (gate)"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "wkv_gathered_prefill_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "wkv_gate_partials_prefill_traffic.json")
 
 
 def parse():
@@ -58,7 +60,7 @@ def kernel_source_digest() -> str:
 
 
 def traffic_record(launch_flops_tokens: int):
-    """HBM bytes per engram_wkv_gathered call (its three kernels) from the
+    """HBM bytes per engram_wkv_gate_partials call (its three kernels) from the
     committed rocprofv3 counter summary, or None if it was taken on a
     different kernel source or workload."""
     try:
@@ -84,7 +86,12 @@ def time_launches(fn, n, stream):
 
 # ------------------------------------------------------------------ profile summaries
 COPY_BYTES = 1 << 30
-FUSED_KERNELS = ("prep_kernel", "wkv_gathered_256", "wkv_gathered_128")
+FUSED_KERNELS = ("prep_kernel", "wkv_gathered_256<3, true, true>", "wkv_gathered_128")
+
+
+def is_fused(k: str) -> bool:
+    """The kernels of one engram_wkv_gate_partials call."""
+    return k in FUSED_KERNELS or k.split("<")[0] in ("prep_kernel", "wkv_gathered_128")
 
 
 def short_name(name: str) -> str:
@@ -130,7 +137,8 @@ def summarize(stats_dir, fetch_dir, write_dir):
     lines = ["# rocprofv3 kernel-trace statistics: Engram prefill forward, T=4096, dim 5120, hc 4",
              "# command (repository root = <repo>):",
              "#   " + cmd_base % ("--kernel-trace --stats", ""),
-             "# engram_wkv_gathered = prep_kernel + wkv_gathered_256<L> + wkv_gathered_128<L>;",
+             "# engram_wkv_gate_partials = prep_kernel + wkv_gathered_256<3, true, true> + wkv_gathered_128<L>",
+             "# (prep_kernel and wkv_gathered_128 also run in the engram_wkv_gathered calls bench times);",
              "# averages include every call (warm-up and cold-clock launches too).",
              "",
              "%-34s %7s %12s %12s %12s %7s" % ("kernel", "calls", "avg_ns", "min_ns", "max_ns", "pct")]
@@ -138,21 +146,20 @@ def summarize(stats_dir, fetch_dir, write_dir):
         lines.append("%-34s %7s %12.0f %12s %12s %7s" % (
             short_name(r["Name"]), r["Calls"], float(r["AverageNs"]), r["MinNs"], r["MaxNs"],
             r["Percentage"]))
-    fused_avg = sum(float(r["AverageNs"]) for r in rows
-                    if short_name(r["Name"]).split("<")[0] in FUSED_KERNELS)
+    fused_avg = sum(float(r["AverageNs"]) for r in rows if is_fused(short_name(r["Name"])))
     # medians from the trace: robust to the few cold-clock launches
     durs = {}
     for r in _csv(stats_dir, "kernel_trace.csv"):
         k = short_name(r["Kernel_Name"])
-        if k.split("<")[0] in FUSED_KERNELS or k.startswith(("gate_kernel", "hash_kernel")):
+        if is_fused(k) or k.startswith(("gate_kernel", "hash_kernel")):
             durs.setdefault(k, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     med = {k: sorted(v)[len(v) // 2] for k, v in durs.items()}
     lines.append("")
     lines.append("# median ns per kernel (kernel trace): " +
                  ", ".join("%s %d" % (k, v) for k, v in sorted(med.items())))
-    lines.append("# engram_wkv_gathered per call: sum of averages %.1f us, sum of medians %.1f us"
+    lines.append("# engram_wkv_gate_partials per call: sum of averages %.1f us, sum of medians %.1f us"
                  % (fused_avg / 1e3,
-                    sum(v for k, v in med.items() if k.split("<")[0] in FUSED_KERNELS) / 1e3))
+                    sum(v for k, v in med.items() if is_fused(k)) / 1e3))
     open(os.path.join(ROOT, "profiles", "engram_prefill_T4096_kernel_stats.txt"), "w").write(
         "\n".join(lines) + "\n")
 
@@ -177,15 +184,15 @@ def summarize(stats_dir, fetch_dir, write_dir):
         f, w_ = fetch.get(k, 0.0), write.get(k, 0.0)
         lines.append("%-26s %14.1f %14.1f %12.1f %12.1f" % (k, f, w_, f * 1024 * fs / 1e6,
                                                             w_ * 1024 * ws / 1e6))
-        if k.split("<")[0] in FUSED_KERNELS:
+        if is_fused(k):
             total["fetch"] += f * 1024 * fs
             total["write"] += w_ * 1024 * ws
     lines.append("# * scaled by the calibration copy; MB = 1e6 bytes.")
-    lines.append("# engram_wkv_gathered per call: fetch %.1f MB + write %.1f MB" %
+    lines.append("# engram_wkv_gate_partials per call: fetch %.1f MB + write %.1f MB" %
                  (total["fetch"] / 1e6, total["write"] / 1e6))
     open(os.path.join(ROOT, "profiles", "engram_prefill_T4096_traffic.txt"), "w").write(
         "\n".join(lines) + "\n")
-    rec = {"kernel": "engram_wkv_gathered (" + " + ".join(FUSED_KERNELS) + ")",
+    rec = {"kernel": "engram_wkv_gate_partials (" + " + ".join(FUSED_KERNELS) + ")",
            "workload": "prefill T=4096 dim 5120 hc 4", "tokens": tokens,
            "source_digest": kernel_source_digest(),
            "fetch_bytes_per_launch": int(total["fetch"]),
@@ -248,18 +255,29 @@ def main():
     tokens_per_s = n_tok / sec
 
     # ---- per-stage launch times (each stage alone, same inputs, same stream);
-    # the forward runs hash -> wkv_gathered -> gate_add; gather and wkv are
-    # the unfused alternative, timed for comparison
+    # the forward runs hash -> wkv_gate_partials -> gate_from_partials; the
+    # other calls are the less fused alternatives, timed for comparison
+    if not ge.engram_gate_partials_supported(g, n_tok):
+        raise SystemExit("the fully fused prefill path does not apply to this workload")
     hid = ge.engram_hash(g, tables, ids)
     rows = ge.engram_gather(g, table, scales, hid)
     kv = ge.engram_wkv(g, rows, w)
     scratch = torch.empty(ge.engram_wkv_gathered_scratch_size(g, n_tok), dtype=torch.uint8,
                           device=dev)
+    xf = x.reshape(n_tok, cfg.hc_mult, cfg.dim)
+    v, part = ge.engram_wkv_gate_partials(g, table, scales, hid, w, xf, q, k, scratch=scratch)
+    outf = out.reshape(n_tok, cfg.hc_mult, cfg.dim)
+    ge.engram_gate_from_partials(g, xf, v, part, mask=mask, out=outf)
     ge.engram_wkv_gathered(g, table, scales, hid, w, kv=kv, scratch=scratch)
     ge.engram_gate_add(g, x, kv, q, k, mask=mask, out=out)
     torch.cuda.synchronize()
     reps = max(args.steps, 10)
     st_hash = time_launches(lambda: ge.engram_hash(g, tables, ids, hash_ids=hid), reps, stream)
+    st_proj = time_launches(
+        lambda: ge.engram_wkv_gate_partials(g, table, scales, hid, w, xf, q, k, v=v, part=part,
+                                            scratch=scratch), reps, stream)
+    st_pgate = time_launches(
+        lambda: ge.engram_gate_from_partials(g, xf, v, part, mask=mask, out=outf), reps, stream)
     st_gather = time_launches(lambda: ge.engram_gather(g, table, scales, hid, rows=rows), reps, stream)
     st_wkv = time_launches(lambda: ge.engram_wkv(g, rows, w, kv=kv), reps, stream)
     st_fused = time_launches(
@@ -270,9 +288,11 @@ def main():
 
     flops_per_token = 2 * g.K * g.N
     wkv_flops = flops_per_token * n_tok
-    achieved = wkv_flops / st_fused / 1e12
+    achieved = wkv_flops / st_proj / 1e12
     traffic = traffic_record(n_tok)
-    gate_bytes = n_tok * (2 * g.hc_mult * g.dim * 2 + g.N * 2)
+    # the gate from partials: x and v read, out written, partial pairs read
+    gate_bytes = n_tok * (2 * g.hc_mult * g.dim * 2 + g.dim * 2 +
+                          g.hc_mult * (g.dim // 128) * 8)
     rec = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),
@@ -289,17 +309,20 @@ def main():
         "config": {"workload": "Engram prefill forward, B=1 T=4096, dim=5120 hc=4, 24 hash cols x "
                                "head_dim 64 (wkv 1536->25600), 25,160,950-row fp8 e4m3 table",
                    "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
-        "roofline": {"kernel": "engram_wkv_gathered", "bound": "mfma",
+        "roofline": {"kernel": "engram_wkv_gate_partials", "bound": "mfma",
                      "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
         "stages_us": {"hash": round(st_hash * 1e6, 2),
-                      "wkv_gathered": round(st_fused * 1e6, 2),
-                      "gate_add": round(st_gate * 1e6, 2),
-                      "unfused_gather": round(st_gather * 1e6, 2),
-                      "unfused_wkv": round(st_wkv * 1e6, 2)},
-        "gate_hbm": {"achieved": round(gate_bytes / st_gate / 1e9, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(gate_bytes / st_gate / 1e9 / PEAK_HBM_GBS, 4)},
+                      "wkv_gate_partials": round(st_proj * 1e6, 2),
+                      "gate_from_partials": round(st_pgate * 1e6, 2),
+                      "alt_wkv_gathered": round(st_fused * 1e6, 2),
+                      "alt_gate_add": round(st_gate * 1e6, 2),
+                      "alt_gather": round(st_gather * 1e6, 2),
+                      "alt_wkv": round(st_wkv * 1e6, 2)},
+        "gate_hbm": {"kernel": "engram_gate_from_partials",
+                     "achieved": round(gate_bytes / st_pgate / 1e9, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gate_bytes / st_pgate / 1e9 / PEAK_HBM_GBS, 4)},
         "wall_s": round(wall, 3),
     }
 

@@ -199,7 +199,7 @@ engram_status engram_gate_from_partials(const engram_geometry* g, const uint16_t
 }
 
 size_t engram_forward_workspace_size(const engram_geometry* g, int64_t n_tok) {
-    if (engram_check_geometry(g) != ENGRAM_OK || n_tok < 0) return 0;
+    if (engram_check_geometry(g) != ENGRAM_OK || n_tok <= 0) return 0;
     const Geom gg = engram::make_geom(*g);
     const size_t rows = (size_t)n_tok * gg.K * sizeof(uint16_t);
     const size_t scl = engram::gathered_scratch_bytes(gg, n_tok);

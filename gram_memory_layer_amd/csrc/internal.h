@@ -56,6 +56,7 @@ struct GatePartials {
     const uint16_t* k;  // [hc, dim] bf16
     float2* part;       // [M, hc, dim / 128] (sum key^2, sum (h*w)*key)
     int dim, hc;
+    const float* wqk;   // [hc, dim] q*k in fp32 (filled by the launcher)
 };
 
 // number of compute units of the current device (cached)

@@ -55,14 +55,21 @@ __device__ __forceinline__ float scale_of(uint32_t c) {
 }
 
 // One thread per (column c, padded row m), m fastest.  Padding rows m >= M
-// get kBadRow and zero scales.
+// get kBadRow and zero scales.  With q and k given, the threads also write
+// wqk = q*k in fp32 (exact: two 8-bit significands) for the gate partials.
 __global__ void __launch_bounds__(256) prep_kernel(const int32_t* __restrict__ hash_ids,
                                                    int n_cols, int64_t M, int64_t m_pad,
                                                    const uint8_t* __restrict__ scales,
                                                    int64_t num_rows, uint32_t* __restrict__ aoff,
                                                    float2* __restrict__ scl,
-                                                   uint32_t* __restrict__ err) {
+                                                   uint32_t* __restrict__ err,
+                                                   const uint16_t* __restrict__ q,
+                                                   const uint16_t* __restrict__ k,
+                                                   float* __restrict__ wqk, int nqk) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (wqk)
+        for (int64_t j = i; j < nqk; j += (int64_t)gridDim.x * blockDim.x)
+            wqk[j] = __uint_as_float((uint32_t)q[j] << 16) * __uint_as_float((uint32_t)k[j] << 16);
     if (i >= (int64_t)n_cols * m_pad) return;
     const int c = (int)(i / m_pad);
     const int64_t m = i - (int64_t)c * m_pad;
@@ -108,10 +115,10 @@ using IC = std::integral_constant<int, V>;
 //     point, so neither the start-up latency of a tile nor its stores stall
 //     the matrix pipe for long.  The last tile loads its own first k-tiles a
 //     second time (harmless; they land before the workgroup ends).
-//   gp.x != nullptr (persistent only): tiles of key columns (n0 < hc*dim)
+//   G (persistent only, gp set): tiles of key columns (n0 < hc*dim)
 //     end in the gate's partial sums instead of a store; value columns go to
 //     C at column n - hc*dim.
-template <int BT, int WMV, int WNV, int L, bool P>
+template <int BT, int WMV, int WNV, int L, bool P, bool G = false>
 __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
                                               const float2* __restrict__ scl, int n_cols,
                                               int64_t m_pad, const uint8_t* __restrict__ table,
@@ -401,47 +408,58 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
             return gq < BT / 16 ? (uint32_t)((gq * G_NS + 2) * 1024)
                                 : (uint32_t)(OFF_W + ((gq - BT / 16) * G_NS + 2) * 1024);
         };
-        const int kcols = gp.x ? gp.hc * gp.dim : 0;  // key columns: reduced, not stored
+        const int kcols = G ? gp.hc * gp.dim : 0;  // key columns: reduced, not stored
         // Key tile: per row, the sums over this wave's 128 columns of key^2
         // and (h*w)*key, the key rounded to bf16 first; products are rounded
         // before they are added (no fused multiply-add), each lane sums its
         // 64 values in a fixed order and adds the other lane half's.
         auto gate_partials = [&]() {
 #pragma clang fp contract(off)
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            typedef float f32x4 __attribute__((ext_vector_type(4)));
             const int s = n0c / gp.dim, f0 = n0c - s * gp.dim + wn * WN;
             const int nq = gp.dim >> 7;
             const __amdgpu_buffer_rsrc_t rx =
                 make_rsrc(gp.x, (uint32_t)(M * gp.hc * gp.dim * 2));  // rows past M read 0
-            const __amdgpu_buffer_rsrc_t rq = make_rsrc(gp.q, (uint32_t)(gp.hc * gp.dim * 2));
-            const __amdgpu_buffer_rsrc_t rk = make_rsrc(gp.k, (uint32_t)(gp.hc * gp.dim * 2));
-            const uint32_t qk0 = (uint32_t)((s * gp.dim + f0) * 2);
+            // this wave's 128 values of q*k, staged in its first stage-2 block
+            // (stage 2 is unused here: key tiles store nothing)
+            const uint32_t wl = blk(0);
+            if (lane < 32)
+                *reinterpret_cast<uint4*>(smem + wl + lane * 16) =
+                    *reinterpret_cast<const uint4*>(gp.wqk + s * gp.dim + f0 + lane * 4);
 #pragma unroll
             for (int i = 0; i < TI; ++i) {
                 const int64_t m = (int64_t)m0c + wm * WM + i * 32 + lrow;
                 const uint32_t xr = (uint32_t)(((m * gp.hc + s) * gp.dim + f0) * 2);
+                // all of the row's h values for this lane first (one round trip)
+                u32x2 hx[TJ * 4];
+#pragma unroll
+                for (int j = 0; j < TJ; ++j)
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4)
+                        hx[j * 4 + g4] = __builtin_amdgcn_raw_buffer_load_b64(
+                            rx, xr + (uint32_t)(j * 32 + 8 * g4 + 4 * lhalf) * 2, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
                 float skk = 0.0f, shwk = 0.0f;
 #pragma unroll
                 for (int j = 0; j < TJ; ++j)
 #pragma unroll
                     for (int g4 = 0; g4 < 4; ++g4) {
-                        const uint32_t nl = (uint32_t)(j * 32 + 8 * g4 + 4 * lhalf) * 2;
-                        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-                        const u32x2 hx = __builtin_amdgcn_raw_buffer_load_b64(rx, xr + nl, 0, 0);
-                        const u32x2 qq = __builtin_amdgcn_raw_buffer_load_b64(rq, qk0 + nl, 0, 0);
-                        const u32x2 kk = __builtin_amdgcn_raw_buffer_load_b64(rk, qk0 + nl, 0, 0);
+                        const int nl = j * 32 + 8 * g4 + 4 * lhalf;
+                        const f32x4 ww = *reinterpret_cast<const f32x4*>(smem + wl + nl * 4);
                         const uint32_t kb[2] = {
                             pack_bf16(acc[j][i][4 * g4 + 0], acc[j][i][4 * g4 + 1]),
                             pack_bf16(acc[j][i][4 * g4 + 2], acc[j][i][4 * g4 + 3])};
+                        const u32x2 h2 = hx[j * 4 + g4];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int sh = (e & 1) ? 0 : 16;  // low half first
-                            const uint32_t hb = hx[e >> 1], qb = qq[e >> 1], kw = kk[e >> 1];
                             const float key = __uint_as_float((kb[e >> 1] << sh) & 0xFFFF0000u);
-                            const float h = __uint_as_float((hb << sh) & 0xFFFF0000u);
-                            const float w = __uint_as_float((qb << sh) & 0xFFFF0000u) *
-                                            __uint_as_float((kw << sh) & 0xFFFF0000u);
-                            skk += key * key;
-                            shwk += (h * w) * key;
+                            const float h = __uint_as_float((h2[e >> 1] << sh) & 0xFFFF0000u);
+                            // key^2 is exact in fp32, so the fused form rounds the
+                            // same sum; (h*w)*key is rounded before the add
+                            skk = __builtin_fmaf(key, key, skk);
+                            shwk += (h * ww[e]) * key;
                         }
                     }
                 skk += __shfl_xor(skk, 32, 64);
@@ -449,9 +467,12 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
                 if (lhalf == 0 && m < M)
                     gp.part[(m * gp.hc + s) * nq + (f0 >> 7)] = make_float2(skk, shwk);
             }
+            // the next tile's DMA may refill stage 2 only after this wave's w reads
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            asm volatile("s_barrier" ::: "memory");
         };
         auto epilogue = [&]() {
-            if (gp.x && n0c < kcols) {
+            if (G && n0c < kcols) {
                 gate_partials();
                 return;
             }
@@ -566,15 +587,15 @@ constexpr int SMEM128 = (128 / 16) * G_NS * 1024 + 4 * G_NS * 256 + (128 / 8) * 
 static_assert(SMEM256 <= 160 * 1024, "LDS budget");
 static_assert(8 * 128 * 128 <= SMEM256 && 4 * 64 * 128 <= SMEM128, "epilogue staging fits the ring");
 
-template <int L, bool P>
+template <int L, bool P, bool G>
 __global__ void __launch_bounds__(512, 1)
 wkv_gathered_256(const uint32_t* __restrict__ aoff, const float2* __restrict__ scl, int n_cols,
                  int64_t m_pad, const uint8_t* __restrict__ table, int64_t num_rows,
                  const uint16_t* __restrict__ W, int64_t M, int N, uint16_t* __restrict__ C,
                  int64_t ldc, int tiles_m, int tiles_n, int per_xcd, GatePartials gp) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM256];
-    gathered_tile<256, 4, 2, L, P>(aoff, scl, n_cols, m_pad, table, num_rows, W, M, N, C, ldc,
-                                   tiles_m, tiles_n, per_xcd, gp, smem);
+    gathered_tile<256, 4, 2, L, P, G>(aoff, scl, n_cols, m_pad, table, num_rows, W, M, N, C, ldc,
+                                      tiles_m, tiles_n, per_xcd, gp, smem);
 }
 
 template <int L>
@@ -599,7 +620,7 @@ hipError_t run_gathered_l(int bt, const uint32_t* aoff, const float2* scl, int n
     const int total = tiles_m * tiles_n;
     const int per_xcd = (total + N_XCD - 1) / N_XCD;
     if (bt == 256)
-        wkv_gathered_256<L, false><<<dim3(per_xcd * N_XCD), dim3(512), 0, s>>>(
+        wkv_gathered_256<L, false, false><<<dim3(per_xcd * N_XCD), dim3(512), 0, s>>>(
             aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, tiles_m, tiles_n, per_xcd,
             GatePartials{});
     else
@@ -634,18 +655,27 @@ hipError_t run_persistent(const uint32_t* aoff, const float2* scl, int n_cols, i
     const int per_xcd = (total + N_XCD - 1) / N_XCD;
     int grid = cus / N_XCD * N_XCD;
     if (grid > per_xcd * N_XCD) grid = per_xcd * N_XCD;
-    wkv_gathered_256<3, true><<<dim3(grid), dim3(512), 0, s>>>(
-        aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, tiles_m, tiles_n, per_xcd, gp);
+    if (gp.x)
+        wkv_gathered_256<3, true, true><<<dim3(grid), dim3(512), 0, s>>>(
+            aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, tiles_m, tiles_n, per_xcd,
+            gp);
+    else
+        wkv_gathered_256<3, true, false><<<dim3(grid), dim3(512), 0, s>>>(
+            aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, tiles_m, tiles_n, per_xcd,
+            gp);
     return hipGetLastError();
 }
 
 int64_t padded_rows(int64_t M) { return (M + 255) / 256 * 256; }
 
 hipError_t launch_prep(const Geom& g, const int32_t* hash_ids, const uint8_t* scales, int64_t M,
-                       int64_t m_pad, uint32_t* aoff, float2* scl, uint32_t* err, hipStream_t s) {
+                       int64_t m_pad, uint32_t* aoff, float2* scl, uint32_t* err, hipStream_t s,
+                       const uint16_t* q = nullptr, const uint16_t* k = nullptr,
+                       float* wqk = nullptr) {
     const int64_t total = (int64_t)g.n_cols * m_pad;
     prep_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s>>>(
-        hash_ids, g.n_cols, M, m_pad, scales, g.num_embeddings, aoff, scl, err);
+        hash_ids, g.n_cols, M, m_pad, scales, g.num_embeddings, aoff, scl, err, q, k, wqk,
+        g.hc * g.dim);
     return hipGetLastError();
 }
 
@@ -683,9 +713,10 @@ bool gathered_supported(const Geom& g, int64_t M) {
            (int64_t)g.n_cols * padded_rows(M) * 8 < ((int64_t)1 << 31);
 }
 
-// aoff (uint32) then scl (2 x fp32) per (hash column, padded row)
+// aoff (uint32) then scl (2 x fp32) per (hash column, padded row), then
+// q*k in fp32 per (stream, feature) for the gate partials
 size_t gathered_scratch_bytes(const Geom& g, int64_t M) {
-    return (size_t)g.n_cols * (size_t)padded_rows(M) * 12;
+    return (size_t)g.n_cols * (size_t)padded_rows(M) * 12 + (size_t)g.hc * g.dim * 4;
 }
 
 // Same tiling policy as the bf16 projection: 256 x 256 tiles over the widest
@@ -737,13 +768,16 @@ hipError_t launch_wkv_gate_partials(const Geom& g, const int32_t* hash_ids, cons
     const int64_t m_pad = padded_rows(M);
     uint32_t* aoff = reinterpret_cast<uint32_t*>(scratch);
     float2* scl = reinterpret_cast<float2*>(aoff + (int64_t)g.n_cols * m_pad);
-    hipError_t e = launch_prep(g, hash_ids, scales, M, m_pad, aoff, scl, err, s);
+    float* wqk = reinterpret_cast<float*>(scl + (int64_t)g.n_cols * m_pad);
+    hipError_t e = launch_prep(g, hash_ids, scales, M, m_pad, aoff, scl, err, s, gp.q, gp.k, wqk);
     if (e != hipSuccess) return e;
     const int cus = cu_count();
     const int nbig = big_columns(M, g.N, cus);
     const int kcols = g.hc * g.dim;
+    GatePartials gpw = gp;
+    gpw.wqk = wqk;
     e = run_persistent(aoff, scl, g.n_cols, m_pad, table, g.num_embeddings, w, M, nbig, v, g.dim,
-                       cus, gp, s);
+                       cus, gpw, s);
     if (e != hipSuccess || nbig >= g.N) return e;
     return run_gathered(128, aoff, scl, g.n_cols, m_pad, table, g.num_embeddings,
                         w + (int64_t)nbig * g.K, M, g.N - nbig, v + (nbig - kcols), g.dim, s);

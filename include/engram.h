@@ -134,7 +134,7 @@ engram_status engram_wkv(const engram_geometry* g, const uint16_t* a, const uint
  *   table, scales, hash_ids as in engram_gather; w, kv as in engram_wkv.
  *   scratch  device memory of engram_wkv_gathered_scratch_size(g, M) bytes,
  *            256-byte aligned (row offsets and scales regrouped per hash
- *            column, 12 bytes per position and column);
+ *            column, 12 bytes per position and column, and q*k in fp32);
  *            contents on entry do not matter.
  * An id outside [0, num_embeddings) reads as a zero row and sets
  * ENGRAM_ERRBIT_ROW in *err (if err is not NULL). */

@@ -90,8 +90,8 @@ def test_fused_projection_host_checks():
     g = good()
     fake = C.c_void_p(1 << 20)
     need = ge.engram_wkv_gathered_scratch_size(g, 4096)
-    assert need == 24 * 4096 * 12
-    assert ge.engram_wkv_gathered_scratch_size(g, 1) == 24 * 256 * 12
+    assert need == 24 * 4096 * 12 + 4 * 5120 * 4
+    assert ge.engram_wkv_gathered_scratch_size(g, 1) == 24 * 256 * 12 + 4 * 5120 * 4
 
     def call(g=g, M=16, scratch=fake, nbytes=1 << 30, table=fake):
         return lib.engram_wkv_gathered(C.byref(g), table, fake, fake, M, fake, fake, scratch,
