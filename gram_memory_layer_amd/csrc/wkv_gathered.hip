@@ -144,16 +144,37 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
     // the end of the sequence)
     const int xcd = blockIdx.x % N_XCD, slot = blockIdx.x / N_XCD;
     const int nwg = gridDim.x / N_XCD;
+    // Persistent order.  Plain projection: each XCD walks its contiguous range
+    // of tile numbers.  With the gate partials (key tiles cost more than value
+    // tiles): round q of the machine takes tile numbers q*grid .. q*grid+grid-1,
+    // the key tiles first, so every workgroup gets the same mix; within a
+    // round an XCD's workgroups take consecutive numbers (shared panels).
+    const int n_key = G ? (gp.hc * gp.dim) / BT : 0;  // key column tiles
+    auto tile_num = [&](int q) {
+        return G ? q * (int)gridDim.x + xcd * nwg + slot : xcd * per_xcd + slot + q * nwg;
+    };
     auto tile_valid = [&](int q) {
+        if constexpr (G) return tile_num(q) < tiles_m * tiles_n;
         const int idx = slot + q * nwg;
         return idx < per_xcd && xcd * per_xcd + idx < tiles_m * tiles_n;
+    };
+    auto tile_coords = [&](int q, int* mt, int* nt) {
+        const int t = tile_num(q);
+        if (G && t < tiles_m * n_key) {
+            tile_at<G_GROUP_M>(t, tiles_m, n_key, mt, nt);
+        } else if (G) {
+            tile_at<G_GROUP_M>(t - tiles_m * n_key, tiles_m, tiles_n - n_key, mt, nt);
+            *nt += n_key;
+        } else {
+            tile_at<G_GROUP_M>(t, tiles_m, tiles_n, mt, nt);
+        }
     };
     int m0c, n0c, m0n, n0n;
     {
         int mt, nt;
         if constexpr (P) {
             if (!tile_valid(0)) return;
-            tile_at<G_GROUP_M>(xcd * per_xcd + slot, tiles_m, tiles_n, &mt, &nt);
+            tile_coords(0, &mt, &nt);
         } else {
             if (!tile_of<G_GROUP_M>(blockIdx.x, per_xcd, tiles_m, tiles_n, &mt, &nt)) return;
         }
@@ -163,7 +184,7 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
     auto set_next = [&](int q) {
         if (tile_valid(q)) {
             int mt, nt;
-            tile_at<G_GROUP_M>(xcd * per_xcd + slot + q * nwg, tiles_m, tiles_n, &mt, &nt);
+            tile_coords(q, &mt, &nt);
             m0n = mt * BT;
             n0n = nt * BT;
         } else {
