@@ -239,9 +239,11 @@ engram_status engram_forward(const engram_geometry* g, const engram_hash_tables*
     }
     uint16_t* kv = (uint16_t*)ws;
     hipStream_t s = (hipStream_t)stream;
-    // the fused gather + projection where its layout applies and the tiled
-    // path runs (prefill-sized batches); gather then projection otherwise
-    const bool fused = n_tok >= 1024 && aligned16(table) && engram::gathered_supported(gg, n_tok);
+    // the fused gather + projection where its layout applies: 256-wide tiles
+    // for prefill-sized batches, 64-wide ones for decode-sized batches;
+    // gather then projection in between and otherwise
+    const bool fused = (n_tok >= 1024 || n_tok <= 256) && aligned16(table) &&
+                       engram::gathered_supported(gg, n_tok);
     hipError_t e = engram::launch_hash(gg, *t, state, ids, B, T, hash_ids, err, s);
     if (fused && engram::gate_partials_supported(gg, n_tok)) {
         // fully fused: the projection reduces the key columns into the gate's

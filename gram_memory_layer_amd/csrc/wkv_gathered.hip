@@ -631,6 +631,22 @@ wkv_gathered_128(const uint32_t* __restrict__ aoff, const float2* __restrict__ s
                                        tiles_m, tiles_n, per_xcd, none, smem);
 }
 
+// decode-sized batches: 64 x 64 tiles, two waves of 32 x 64, so that a
+// 64-position step still spreads the weight stream over 400 workgroups
+constexpr int SMEM64 = (64 / 16) * G_NS * 1024 + 2 * G_NS * 256 + (64 / 8) * G_NS * 1024;
+
+template <int L>
+__global__ void __launch_bounds__(128)
+wkv_gathered_64(const uint32_t* __restrict__ aoff, const float2* __restrict__ scl, int n_cols,
+                int64_t m_pad, const uint8_t* __restrict__ table, int64_t num_rows,
+                const uint16_t* __restrict__ W, int64_t M, int N, uint16_t* __restrict__ C,
+                int64_t ldc, int tiles_m, int tiles_n, int per_xcd) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM64];
+    const GatePartials none{};
+    gathered_tile<64, 2, 1, L, false>(aoff, scl, n_cols, m_pad, table, num_rows, W, M, N, C, ldc,
+                                      tiles_m, tiles_n, per_xcd, none, smem);
+}
+
 template <int L>
 hipError_t run_gathered_l(int bt, const uint32_t* aoff, const float2* scl, int n_cols,
                           int64_t m_pad, const uint8_t* table, int64_t num_rows,
@@ -644,6 +660,9 @@ hipError_t run_gathered_l(int bt, const uint32_t* aoff, const float2* scl, int n
         wkv_gathered_256<L, false, false><<<dim3(per_xcd * N_XCD), dim3(512), 0, s>>>(
             aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, tiles_m, tiles_n, per_xcd,
             GatePartials{});
+    else if (bt == 64)
+        wkv_gathered_64<L><<<dim3(per_xcd * N_XCD), dim3(128), 0, s>>>(
+            aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, tiles_m, tiles_n, per_xcd);
     else
         wkv_gathered_128<L><<<dim3(per_xcd * N_XCD), dim3(256), 0, s>>>(
             aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, tiles_m, tiles_n, per_xcd);
@@ -755,6 +774,9 @@ hipError_t launch_wkv_gathered(const Geom& g, const int32_t* hash_ids, const uin
         hipError_t e = launch_prep(g, hash_ids, scales, M, m_pad, aoff, scl, err, s);
         if (e != hipSuccess) return e;
     }
+    if (M <= 256)  // decode-sized: the weight stream dominates; small tiles, many workgroups
+        return run_gathered(64, aoff, scl, g.n_cols, m_pad, table, g.num_embeddings, w, M, g.N,
+                            kv, g.N, s);
     const int N = g.N;
     const int cus = cu_count();
     const int nbig = big_columns(M, N, cus);
