@@ -43,6 +43,9 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run 3 plain device copies of exactly 1 GiB (a known-size kernel "
                         "against which HBM byte counters are scaled)")
+    p.add_argument("--workload", choices=("prefill", "decode"), default="prefill",
+                   help="prefill (the default and the headline line) or decode: 128 steps "
+                        "of 64 sequences after a 512-token prefill, replayed as one graph")
     p.add_argument("--summarize", nargs=3, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR"),
                    help="no GPU work: turn the CSV output of three rocprofv3 runs of this "
                         "script (--kernel-trace --stats; --pmc FETCH_SIZE; --pmc WRITE_SIZE, "
@@ -214,6 +217,9 @@ def main():
               "Engram path is measured per GPU (see DESIGN.md for how it would shard).",
               file=sys.stderr)
         sys.exit(2)
+    if args.workload == "decode":
+        decode(args)
+        return
     import numpy as np
     import torch
 
@@ -339,6 +345,93 @@ def main():
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(cfg, t, table, scales, w, q, k, x, ids_np, mask,
                                            args.cpu_sample)
+    print(json.dumps(rec), flush=True)
+
+
+def decode(args):
+    """Decode: B=64 sequences, 128 steps of one token after a 512-token
+    prefill of the hash state.  The 128 forwards are captured once in a graph
+    (the library allocates nothing and needs no host synchronisation) and the
+    graph is replayed; one step = one forward of 64 tokens.  The roofline is
+    the projection's weight stream: W (78.6 MB) + the fp8 rows + kv per step
+    over the event-timed engram_wkv_gathered call at M = 64."""
+    import torch
+
+    import gram_memory_layer_amd as ge
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = synth.config("decode")
+    t = synth.hash_tables(cfg)
+    g = ge.Geometry.make(cfg.dim, cfg.hc_mult, cfg.max_ngram_size, cfg.n_heads, cfg.head_dim,
+                         t["num_embeddings"], cfg.vocab, cfg.pad_id, cfg.norm_eps)
+    tables = {k: torch.from_numpy(t[k]).to(dev) for k in ("token_map", "mult", "prime", "offset")}
+    table, scales = synth.embedding_table(cfg, t["num_embeddings"], dev)
+    w = synth.wkv_weight(cfg, dev)
+    q, k = synth.qk_weights(cfg, dev)
+    B, S = cfg.B, cfg.steps
+    state0 = torch.full((B, cfg.max_ngram_size - 1), cfg.pad_id, dtype=torch.int32, device=dev)
+    ge.engram_hash(g, tables, torch.from_numpy(synth.token_ids(cfg, B, cfg.prefill,
+                                                               name="prefill_ids")).to(dev),
+                   state=state0)
+    step_ids = synth.token_ids(cfg, B, S, name="step_ids")
+    ids = [torch.from_numpy(step_ids[:, s:s + 1].copy()).to(dev) for s in range(S)]
+    xs = [synth.activations(cfg, B, dev, name="x_step%d" % s).reshape(B, 1, cfg.hc_mult, cfg.dim)
+          for s in range(8)]
+    out = torch.empty_like(xs[0])
+    ws = torch.empty(ge.engram_forward_workspace_size(g, B), dtype=torch.uint8, device=dev)
+    state = state0.clone()
+
+    def steps():
+        for s in range(S):
+            ge.engram_forward(g, tables, table, scales, w, q, k, xs[s % 8], ids[s], state=state,
+                              out=out, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        steps()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        steps()
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(max(args.warmup // 10, 2)):
+        graph.replay()
+    torch.cuda.synchronize()
+    reps = max(args.steps // 10, 3)
+    t0 = time.perf_counter()
+    sec = time_launches(graph.replay, reps, stream) / S  # per step
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    eager = time_launches(steps, 2, stream) / S
+
+    hid = ge.engram_hash(g, tables, ids[0])
+    kv = torch.empty((B, g.N), dtype=torch.bfloat16, device=dev)
+    scratch = torch.empty(ge.engram_wkv_gathered_scratch_size(g, B), dtype=torch.uint8, device=dev)
+    ge.engram_wkv_gathered(g, table, scales, hid, w, kv=kv, scratch=scratch)
+    st_proj = time_launches(lambda: ge.engram_wkv_gathered(g, table, scales, hid, w, kv=kv,
+                                                           scratch=scratch), 200, stream)
+    proj_bytes = g.N * g.K * 2 + B * g.n_hash_cols * (64 + 2) + B * g.N * 2
+    rec = {
+        "metric": "Engram decode tokens/s @dim5120 hc4 (1 GPU), B=64, 128 steps after 512",
+        "value": round(B / sec, 1), "unit": "tokens/s", "n_gpus": 1, "steps": S * reps,
+        "warmup": max(args.warmup // 10, 2) * S, "ms_per_step": round(sec * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Engram decode, B=64 x 1 token per step, 128 steps replayed as "
+                               "one graph, dim=5120 hc=4, 24 hash cols x head_dim 64",
+                   "global_batch": B, "seq_len": 1, "parallelism": "single GPU"},
+        "roofline": {"kernel": "engram_wkv_gathered (M=64)", "bound": "hbm",
+                     "achieved": round(proj_bytes / st_proj / 1e9, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(proj_bytes / st_proj / 1e9 / PEAK_HBM_GBS, 4),
+                     "traffic": None},
+        "eager_ms_per_step": round(eager * 1e3, 4),
+        "projection_us": round(st_proj * 1e6, 2),
+        "wall_s": round(wall, 3),
+    }
     print(json.dumps(rec), flush=True)
 
 

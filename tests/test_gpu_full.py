@@ -213,6 +213,66 @@ def test_decode_full(ge, dev):
     assert np.array_equal(state.cpu().numpy(), wl.t["token_map"][steps[:, -2:]])
 
 
+def test_decode_graph_replay(ge, dev):
+    # decode steps captured once in a graph and replayed: every replay must
+    # give the eager run's outputs and state bit for bit (the library
+    # allocates nothing and clears nothing with memset, so its launches can
+    # be captured); eager work and synchronisations run between replays
+    wl = Workload(ge, "decode", dev)
+    cfg = wl.cfg
+    B, S = cfg.B, 8
+    pre = torch.from_numpy(synth.token_ids(cfg, B, cfg.prefill, name="prefill_ids")).to(dev)
+    step_ids = synth.token_ids(cfg, B, S, name="step_ids")
+    ids = [torch.from_numpy(step_ids[:, s:s + 1].copy()).to(dev) for s in range(S)]
+    xs = [synth.activations(cfg, B, dev, name="x_step%d" % s).reshape(B, 1, cfg.hc_mult, cfg.dim)
+          for s in range(S)]
+    layer = ge.EngramLayer(wl.g, wl.tables, wl.table, wl.scales, wl.w, wl.q, wl.k)
+    ws = layer.workspace(B)
+    state0 = torch.full((B, cfg.max_ngram_size - 1), cfg.pad_id, dtype=torch.int32, device=dev)
+    ge.engram_hash(wl.g, wl.tables, pre, state=state0)
+
+    def run(state, outs, gates):
+        for s in range(S):
+            ge.engram_forward(wl.g, wl.tables, wl.table, wl.scales, wl.w, wl.q, wl.k, xs[s], ids[s],
+                              state=state, out=outs[s], gate=gates[s], workspace=ws)
+
+    def buffers():
+        return ([torch.empty_like(x) for x in xs],
+                [torch.empty((B, 1, cfg.hc_mult), dtype=torch.float32, device=dev)
+                 for _ in range(S)])
+
+    say("decode graph: eager reference")
+    st_e = state0.clone()
+    out_e, gate_e = buffers()
+    run(st_e, out_e, gate_e)
+    torch.cuda.synchronize()
+
+    st_g = state0.clone()
+    out_g, gate_g = buffers()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(st_g.clone(), out_g, gate_g)  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        run(st_g, out_g, gate_g)
+    for rep in range(3):
+        say("decode graph: replay", rep)
+        st_g.copy_(state0)
+        for o in out_g:
+            o.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(st_g, st_e), rep
+        for s in range(S):
+            assert torch.equal(out_g[s].view(torch.int16), out_e[s].view(torch.int16)), (rep, s)
+            assert torch.equal(gate_g[s], gate_e[s]), (rep, s)
+        _ = (xs[0].float() * 2).sum().item()  # eager work between replays
+
+
 # ------------------------------------------------------------------ gate stress
 def test_gate_stress_full(ge, dev):
     cfg = synth.config("gate_stress")
