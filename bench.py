@@ -260,9 +260,13 @@ def main():
     wall = time.perf_counter() - t0
     tokens_per_s = n_tok / sec
 
-    # ---- per-stage launch times (each stage alone, same inputs, same stream);
-    # the forward runs hash -> wkv_gate_partials -> gate_from_partials; the
-    # other calls are the less fused alternatives, timed for comparison
+    # ---- per-stage launch times (each stage alone, same inputs, same stream).
+    # The forward runs hash_prep_kernel (the hash written straight as the
+    # projection's row offsets and scales, with q*k) -> the projection's
+    # persistent and tail kernels -> gate_from_partials; the stage calls below
+    # are the public entry points (engram_hash writes hash ids, and the
+    # projection call starts with its own prep kernel), plus the less fused
+    # alternatives, timed for comparison
     if not ge.engram_gate_partials_supported(g, n_tok):
         raise SystemExit("the fully fused prefill path does not apply to this workload")
     hid = ge.engram_hash(g, tables, ids)

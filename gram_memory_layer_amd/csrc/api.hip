@@ -244,25 +244,31 @@ engram_status engram_forward(const engram_geometry* g, const engram_hash_tables*
     // gather then projection in between and otherwise
     const bool fused = (n_tok >= 1024 || n_tok <= 256) && aligned16(table) &&
                        engram::gathered_supported(gg, n_tok);
-    hipError_t e = engram::launch_hash(gg, *t, state, ids, B, T, hash_ids, err, s);
     if (fused && engram::gate_partials_supported(gg, n_tok)) {
-        // fully fused: the projection reduces the key columns into the gate's
-        // partial sums and stores only the value; kv's region holds both
+        // fully fused: the hash writes the projection's row offsets and
+        // scales directly; the projection reduces the key columns into the
+        // gate's partial sums and stores only the value; kv's region holds both
         uint16_t* v = kv;
         float2* part = reinterpret_cast<float2*>(
             reinterpret_cast<char*>(kv) + align256((size_t)n_tok * gg.dim * sizeof(uint16_t)));
         const engram::GatePartials gp{x, q, k, part, gg.dim, gg.hc};
+        hipError_t e = engram::launch_hash_prep(gg, *t, state, ids, B, T, scales, q, k, rows, err, s);
         if (e == hipSuccess)
-            e = engram::launch_wkv_gate_partials(gg, hash_ids, table, scales, w, n_tok, gp, v,
-                                                 rows, err, s);
+            e = engram::launch_wkv_gate_partials(gg, nullptr, table, scales, w, n_tok, gp, v, rows,
+                                                 err, s, /*prepared=*/true);
         if (e == hipSuccess)
             e = engram::launch_gate_from_partials(gg, x, v, part, mask, n_tok, out, gate, s);
         return from_hip(e);
     }
+    hipError_t e;
     if (fused) {
+        e = engram::launch_hash_prep(gg, *t, state, ids, B, T, scales, nullptr, nullptr, rows, err,
+                                     s);
         if (e == hipSuccess)
-            e = engram::launch_wkv_gathered(gg, hash_ids, table, scales, w, n_tok, kv, rows, err, s);
+            e = engram::launch_wkv_gathered(gg, nullptr, table, scales, w, n_tok, kv, rows, err, s,
+                                            /*prepared=*/true);
     } else {
+        e = engram::launch_hash(gg, *t, state, ids, B, T, hash_ids, err, s);
         if (e == hipSuccess)
             e = engram::launch_gather(gg, table, scales, hash_ids, n_tok, rows, err, s);
         if (e == hipSuccess) e = engram::launch_wkv(rows, w, n_tok, gg.N, gg.K, kv, s);

@@ -30,6 +30,30 @@ __device__ __forceinline__ uint32_t compressed_at(int p, int b, int T, int n_sta
     return (uint32_t)token_map[tok];
 }
 
+// Hash id of column col at position t of sequence b (the unsigned 64-bit
+// mix, reduced modulo the column's prime and moved by its offset); sets
+// ENGRAM_ERRBIT_HASH and gives -1 when that lands outside the table.
+__device__ __forceinline__ int32_t hash_at(int b, int t, int col, int T, int n_heads,
+                                           int max_ngram, const int32_t* __restrict__ ids,
+                                           const int32_t* __restrict__ token_map,
+                                           const uint64_t* __restrict__ mult,
+                                           const uint64_t* __restrict__ prime,
+                                           const uint64_t* __restrict__ offset,
+                                           const int32_t* __restrict__ state, int vocab,
+                                           int pad_id, int64_t num_embeddings, uint32_t* bad) {
+    const int n = 2 + col / n_heads;
+    const int n_state = max_ngram - 1;
+    uint64_t mix = 0;
+    for (int k = 0; k < n; ++k) {
+        uint32_t c = compressed_at(t - k, b, T, n_state, ids, token_map, state, vocab, pad_id, bad);
+        mix ^= (uint64_t)c * mult[(int64_t)col * max_ngram + k];
+    }
+    const uint64_t h = mix % prime[col] + offset[col];
+    if (h < (uint64_t)num_embeddings) return (int32_t)h;
+    *bad |= ENGRAM_ERRBIT_HASH;
+    return -1;
+}
+
 __global__ void __launch_bounds__(256) hash_kernel(
     const int32_t* __restrict__ token_map, const uint64_t* __restrict__ mult,
     const uint64_t* __restrict__ prime, const uint64_t* __restrict__ offset,
@@ -43,23 +67,50 @@ __global__ void __launch_bounds__(256) hash_kernel(
     const int64_t bt = i / n_cols;
     const int b = (int)(bt / T);
     const int t = (int)(bt % T);
-    const int n = 2 + col / n_heads;
-    const int n_state = max_ngram - 1;
     uint32_t bad = 0;
-    uint64_t mix = 0;
-    for (int k = 0; k < n; ++k) {
-        uint32_t c = compressed_at(t - k, b, T, n_state, ids, token_map, state, vocab, pad_id, &bad);
-        mix ^= (uint64_t)c * mult[(int64_t)col * max_ngram + k];
+    hash_ids[i] = hash_at(b, t, col, T, n_heads, max_ngram, ids, token_map, mult, prime, offset,
+                          state, vocab, pad_id, num_embeddings, &bad);
+    if (bad && err) atomicOr(err, bad);
+}
+
+// The hash, written straight in the form the fused projections read: one
+// thread per (column c, padded row m), m fastest, so the offset and scale
+// stores are coalesced.  Row m = b*T + t; rows past B*T are padding.  A hash
+// outside the table also counts as a bad row, as it does when the ids pass
+// through memory.  When wqk is given, q*k in fp32 as well.
+__global__ void __launch_bounds__(256) hash_prep_kernel(
+    const int32_t* __restrict__ token_map, const uint64_t* __restrict__ mult,
+    const uint64_t* __restrict__ prime, const uint64_t* __restrict__ offset,
+    const int32_t* __restrict__ state, const int32_t* __restrict__ ids, int B, int T,
+    int n_cols, int n_heads, int max_ngram, int vocab, int pad_id, int64_t num_embeddings,
+    const uint8_t* __restrict__ scales, int64_t m_pad, uint32_t* __restrict__ aoff,
+    float2* __restrict__ scl, uint32_t* __restrict__ err, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ k, float* __restrict__ wqk, int nqk) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (wqk)
+        for (int64_t j = i; j < nqk; j += (int64_t)gridDim.x * blockDim.x)
+            wqk[j] = __uint_as_float((uint32_t)q[j] << 16) * __uint_as_float((uint32_t)k[j] << 16);
+    if (i >= (int64_t)n_cols * m_pad) return;
+    const int col = (int)(i / m_pad);
+    const int64_t m = i - (int64_t)col * m_pad;
+    uint32_t off = kBadRowOffset;
+    float2 sc = make_float2(0.0f, 0.0f);
+    uint32_t bad = 0;
+    if (m < (int64_t)B * T) {
+        const int b = (int)(m / T);
+        const int t = (int)(m - (int64_t)b * T);
+        const int32_t id = hash_at(b, t, col, T, n_heads, max_ngram, ids, token_map, mult, prime,
+                                   offset, state, vocab, pad_id, num_embeddings, &bad);
+        if (id >= 0) {
+            off = (uint32_t)id * 64u;
+            sc = make_float2(e8m0_scale(scales[2 * (int64_t)id]),
+                             e8m0_scale(scales[2 * (int64_t)id + 1]));
+        } else {
+            bad |= ENGRAM_ERRBIT_ROW;
+        }
     }
-    uint64_t h = mix % prime[col] + offset[col];
-    int32_t out;
-    if (h < (uint64_t)num_embeddings) {
-        out = (int32_t)h;
-    } else {
-        out = -1;
-        bad |= ENGRAM_ERRBIT_HASH;
-    }
-    hash_ids[i] = out;
+    aoff[i] = off;
+    scl[i] = sc;
     if (bad && err) atomicOr(err, bad);
 }
 
@@ -80,7 +131,31 @@ __global__ void __launch_bounds__(64) state_kernel(const int32_t* __restrict__ t
     for (int j = 0; j < n_state; ++j) state[(int64_t)b * n_state + j] = (int32_t)v[j];
 }
 
+void launch_state(const Geom& g, const engram_hash_tables& t, int32_t* state, const int32_t* ids,
+                  int B, int T, hipStream_t s) {
+    state_kernel<<<dim3((B + 63) / 64), dim3(64), 0, s>>>(t.token_map, ids, B, T, g.max_ngram - 1,
+                                                          g.vocab, g.pad_id, state);
+}
+
 }  // namespace
+
+hipError_t launch_hash_prep(const Geom& g, const engram_hash_tables& t, int32_t* state,
+                            const int32_t* ids, int B, int T, const uint8_t* scales,
+                            const uint16_t* q, const uint16_t* k, void* scratch, uint32_t* err,
+                            hipStream_t s) {
+    const int64_t M = (int64_t)B * T;
+    if (M == 0) return hipSuccess;
+    const GatheredScratch gs = gathered_scratch(g, M, scratch);
+    const int64_t total = (int64_t)g.n_cols * gs.m_pad;
+    hash_prep_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s>>>(
+        t.token_map, t.mult, t.prime, t.offset, state, ids, B, T, g.n_cols, g.n_heads,
+        g.max_ngram, g.vocab, g.pad_id, g.num_embeddings, scales, gs.m_pad, gs.aoff, gs.scl, err,
+        q, k, q ? gs.wqk : nullptr, g.hc * g.dim);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || state == nullptr) return e;
+    launch_state(g, t, state, ids, B, T, s);
+    return hipGetLastError();
+}
 
 hipError_t launch_hash(const Geom& g, const engram_hash_tables& t, int32_t* state,
                        const int32_t* ids, int B, int T, int32_t* hash_ids, uint32_t* err,
@@ -94,8 +169,7 @@ hipError_t launch_hash(const Geom& g, const engram_hash_tables& t, int32_t* stat
         g.max_ngram, g.vocab, g.pad_id, g.num_embeddings, hash_ids, err);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || state == nullptr) return e;
-    state_kernel<<<dim3((B + 63) / 64), dim3(64), 0, s>>>(t.token_map, ids, B, T, g.max_ngram - 1,
-                                                          g.vocab, g.pad_id, state);
+    launch_state(g, t, state, ids, B, T, s);
     return hipGetLastError();
 }
 

@@ -59,15 +59,49 @@ struct GatePartials {
     const float* wqk;   // [hc, dim] q*k in fp32 (filled by the launcher)
 };
 
+// Scratch of the fused projections: per (hash column c, padded row m) the
+// table byte offset of row hash_ids[m][c] (kBadRowOffset, past any table,
+// for a bad id or a padding row: the buffer load then reads zeros) and the
+// row's two block scales as fp32; then q*k in fp32 per (stream, feature).
+constexpr uint32_t kBadRowOffset = 0xFFFFFFC0u;
+__host__ __device__ inline int64_t padded_rows(int64_t M) { return (M + 255) / 256 * 256; }
+struct GatheredScratch {
+    uint32_t* aoff;  // [n_cols][m_pad]
+    float2* scl;     // [n_cols][m_pad]
+    float* wqk;      // [hc * dim]
+    int64_t m_pad;
+};
+GatheredScratch gathered_scratch(const Geom& g, int64_t M, void* base);
+
+// e8m0 code -> fp32 scale 2^(c-127), branch-free (code 0 is the subnormal
+// 2^-127, 255 is NaN)
+__device__ __forceinline__ float e8m0_scale(uint32_t c) {
+    uint32_t b = c << 23;
+    b = c == 0u ? 0x00400000u : b;
+    b = c == 0xFFu ? 0x7FC00000u : b;
+    return __uint_as_float(b);
+}
+
+// Stage 1 straight into the fused projections' scratch (the hash ids
+// themselves are not written): for every position and hash column, the row
+// offset and scales; q*k as well when q is given; the state updated as in
+// launch_hash.
+hipError_t launch_hash_prep(const Geom& g, const engram_hash_tables& t, int32_t* state,
+                            const int32_t* ids, int B, int T, const uint8_t* scales,
+                            const uint16_t* q, const uint16_t* k, void* scratch, uint32_t* err,
+                            hipStream_t s);
+
 // number of compute units of the current device (cached)
 int cu_count();
 
 // projection straight from hash ids (rows gathered as the GEMM's A operand)
 bool gathered_supported(const Geom& g, int64_t M);
 size_t gathered_scratch_bytes(const Geom& g, int64_t M);
+// prepared: the scratch already holds the offsets and scales (launch_hash_prep)
 hipError_t launch_wkv_gathered(const Geom& g, const int32_t* hash_ids, const uint8_t* table,
                                const uint8_t* scales, const uint16_t* w, int64_t M, uint16_t* kv,
-                               void* scratch, uint32_t* err, hipStream_t s);
+                               void* scratch, uint32_t* err, hipStream_t s,
+                               bool prepared = false);
 
 // The same projection with the gate's key reductions in its epilogue (see
 // GatePartials); writes v [M, dim] and gp.part.  Only where
@@ -76,7 +110,7 @@ bool gate_partials_supported(const Geom& g, int64_t M);
 hipError_t launch_wkv_gate_partials(const Geom& g, const int32_t* hash_ids, const uint8_t* table,
                                     const uint8_t* scales, const uint16_t* w, int64_t M,
                                     const GatePartials& gp, uint16_t* v, void* scratch,
-                                    uint32_t* err, hipStream_t s);
+                                    uint32_t* err, hipStream_t s, bool prepared = false);
 
 // Stage 4 from the partial sums: per (token, stream) S_hh from x, S_kk and
 // S_hwk as the fixed-order sum of the dim/128 partials, then g and

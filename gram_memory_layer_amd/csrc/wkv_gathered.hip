@@ -35,7 +35,7 @@ namespace {
 
 constexpr int G_NS = 3;                   // stages in the LDS ring
 constexpr int G_GROUP_M = 4;              // M-tiles per group in the tile order
-constexpr uint32_t kBadRow = 0xFFFFFFC0u;  // >= any table's byte size: the DMA reads zeros
+constexpr uint32_t kBadRow = kBadRowOffset;  // past any table: the DMA reads zeros
 
 // 16-byte slot of logical chunk c (0..3) in a 64-byte LDS row.  A fragment
 // read is one 16-byte chunk of 32 consecutive rows; the XOR term is a
@@ -46,13 +46,6 @@ __device__ __forceinline__ int slot64(int row, int c) {
     return c ^ (((row >> 1) & 3) ^ ((row >> 3) & 1));
 }
 
-// e8m0 code -> fp32 scale 2^(c-127) (code 0 is the subnormal 2^-127, 255 is NaN)
-__device__ __forceinline__ float scale_of(uint32_t c) {
-    uint32_t b = c << 23;
-    b = c == 0u ? 0x00400000u : b;
-    b = c == 0xFFu ? 0x7FC00000u : b;
-    return __uint_as_float(b);
-}
 
 // One thread per (column c, padded row m), m fastest.  Padding rows m >= M
 // get kBadRow and zero scales.  With q and k given, the threads also write
@@ -79,7 +72,8 @@ __global__ void __launch_bounds__(256) prep_kernel(const int32_t* __restrict__ h
         const int32_t id = hash_ids[m * n_cols + c];
         if (id >= 0 && id < num_rows) {
             off = (uint32_t)id * 64u;
-            sc = make_float2(scale_of(scales[2 * (int64_t)id]), scale_of(scales[2 * (int64_t)id + 1]));
+            sc = make_float2(e8m0_scale(scales[2 * (int64_t)id]),
+                             e8m0_scale(scales[2 * (int64_t)id + 1]));
         } else if (err) {
             atomicOr(err, ENGRAM_ERRBIT_ROW);
         }
@@ -706,8 +700,6 @@ hipError_t run_persistent(const uint32_t* aoff, const float2* scl, int n_cols, i
     return hipGetLastError();
 }
 
-int64_t padded_rows(int64_t M) { return (M + 255) / 256 * 256; }
-
 hipError_t launch_prep(const Geom& g, const int32_t* hash_ids, const uint8_t* scales, int64_t M,
                        int64_t m_pad, uint32_t* aoff, float2* scl, uint32_t* err, hipStream_t s,
                        const uint16_t* q = nullptr, const uint16_t* k = nullptr,
@@ -763,14 +755,24 @@ size_t gathered_scratch_bytes(const Geom& g, int64_t M) {
 // column range that fills whole rounds of the machine, 128 x 128 tiles over
 // the rest when they fit in one round.  `scratch` holds
 // gathered_scratch_bytes(g, M) bytes, 256-byte aligned.
+GatheredScratch gathered_scratch(const Geom& g, int64_t M, void* base) {
+    GatheredScratch r;
+    r.m_pad = padded_rows(M);
+    r.aoff = reinterpret_cast<uint32_t*>(base);
+    r.scl = reinterpret_cast<float2*>(r.aoff + (int64_t)g.n_cols * r.m_pad);
+    r.wqk = reinterpret_cast<float*>(r.scl + (int64_t)g.n_cols * r.m_pad);
+    return r;
+}
+
 hipError_t launch_wkv_gathered(const Geom& g, const int32_t* hash_ids, const uint8_t* table,
                                const uint8_t* scales, const uint16_t* w, int64_t M, uint16_t* kv,
-                               void* scratch, uint32_t* err, hipStream_t s) {
+                               void* scratch, uint32_t* err, hipStream_t s, bool prepared) {
     if (M == 0) return hipSuccess;
-    const int64_t m_pad = padded_rows(M);
-    uint32_t* aoff = reinterpret_cast<uint32_t*>(scratch);
-    float2* scl = reinterpret_cast<float2*>(aoff + (int64_t)g.n_cols * m_pad);
-    {
+    const GatheredScratch gs = gathered_scratch(g, M, scratch);
+    const int64_t m_pad = gs.m_pad;
+    uint32_t* aoff = gs.aoff;
+    float2* scl = gs.scl;
+    if (!prepared) {
         hipError_t e = launch_prep(g, hash_ids, scales, M, m_pad, aoff, scl, err, s);
         if (e != hipSuccess) return e;
     }
@@ -805,14 +807,17 @@ bool gate_partials_supported(const Geom& g, int64_t M) {
 hipError_t launch_wkv_gate_partials(const Geom& g, const int32_t* hash_ids, const uint8_t* table,
                                     const uint8_t* scales, const uint16_t* w, int64_t M,
                                     const GatePartials& gp, uint16_t* v, void* scratch,
-                                    uint32_t* err, hipStream_t s) {
+                                    uint32_t* err, hipStream_t s, bool prepared) {
     if (M == 0) return hipSuccess;
     if (!gate_partials_supported(g, M) || gp.dim != g.dim || gp.hc != g.hc) return hipErrorInvalidValue;
-    const int64_t m_pad = padded_rows(M);
-    uint32_t* aoff = reinterpret_cast<uint32_t*>(scratch);
-    float2* scl = reinterpret_cast<float2*>(aoff + (int64_t)g.n_cols * m_pad);
-    float* wqk = reinterpret_cast<float*>(scl + (int64_t)g.n_cols * m_pad);
-    hipError_t e = launch_prep(g, hash_ids, scales, M, m_pad, aoff, scl, err, s, gp.q, gp.k, wqk);
+    const GatheredScratch gs = gathered_scratch(g, M, scratch);
+    const int64_t m_pad = gs.m_pad;
+    uint32_t* aoff = gs.aoff;
+    float2* scl = gs.scl;
+    float* wqk = gs.wqk;
+    hipError_t e = prepared ? hipSuccess
+                            : launch_prep(g, hash_ids, scales, M, m_pad, aoff, scl, err, s, gp.q,
+                                          gp.k, wqk);
     if (e != hipSuccess) return e;
     const int cus = cu_count();
     const int nbig = big_columns(M, g.N, cus);

@@ -237,3 +237,65 @@ def test_gate_from_partials_against_oracle(ge, dev, gp_case):
     os_ = tolerances.check_out(bits(out[ri]), ref_out, xb, kvb[:, cfg.hc_mult * cfg.dim:],
                                gate.cpu().numpy()[rows], ref_gate)
     say("   gate", gs, "out", os_)
+
+
+# ------------------------------------------------------------------ forward = its stages
+# The forward hashes straight into the fused projections' row offsets and
+# scales.  It must give the same out, gate, state and error bits, bit for bit,
+# as the stage calls it stands for, also with bad token ids (flagged, read as
+# the pad id) and a hash column whose slots all fall past the table (flagged,
+# its rows read as zeros).  Cases: the 64-wide fused tiles (n_tok <= 256), the
+# gather + projection in between, the 256-wide fused tiles, and the fully
+# fused path with the gate's sums in the projection.
+FWD_CASES = [((256, 3, 3, 2), 1, 37), ((256, 3, 3, 2), 3, 100), ((256, 3, 3, 2), 1, 1100),
+             ((2048, 4, 3, 3), 1, 4096)]
+
+
+@pytest.mark.parametrize("shape,B,T", FWD_CASES)
+def test_forward_equals_stage_calls(ge, dev, shape, B, T):
+    dim, hc, mx, nh = shape
+    cfg = dataclasses.replace(synth.config("tiny"), dim=dim, hc_mult=hc, max_ngram_size=mx,
+                              n_heads=nh, head_dim=64, scale_codes=(120, 132))
+    wl = Workload(ge, cfg, dev)
+    g = wl.g
+    n = B * T
+    say("forward vs stages", shape, "B", B, "T", T)
+    t = dict(wl.t)
+    t["offset"] = t["offset"].copy()
+    t["offset"][1] += np.uint64(wl.num_emb)          # column 1: every slot past the table
+    tables = {k2: torch.from_numpy(np.ascontiguousarray(t[k2])).to(dev)
+              for k2 in ("token_map", "mult", "prime", "offset")}
+    ids_np = synth.token_ids(cfg, B, T, name="fs")
+    ids_np[0, min(5, T - 1)] = cfg.vocab + 7
+    ids_np[-1, T // 2] = -3
+    ids = torch.from_numpy(ids_np).to(dev)
+    x = synth.activations(cfg, n, dev, name="fsx").reshape(B, T, hc, dim)
+    mask = torch.from_numpy(synth.token_ids(cfg, B, T, name="fsm") % 4 != 0).to(dev)
+    st0 = torch.from_numpy(synth.token_ids(cfg, B, mx - 1, name="fss") % 500).to(dev)
+
+    state_a, err_a = st0.clone(), torch.zeros(1, dtype=torch.int32, device=dev)
+    gate_a = torch.empty((B, T, hc), dtype=torch.float32, device=dev)
+    out_a = ge.engram_forward(g, tables, wl.table, wl.scales, wl.w, wl.q, wl.k, x, ids, mask=mask,
+                              state=state_a, gate=gate_a, err=err_a)
+
+    state_b, err_b = st0.clone(), torch.zeros(1, dtype=torch.int32, device=dev)
+    gate_b = torch.empty((B, T, hc), dtype=torch.float32, device=dev)
+    hid = ge.engram_hash(g, tables, ids, state=state_b, err=err_b).reshape(n, -1)
+    xf = x.reshape(n, hc, dim)
+    if ge.engram_gate_partials_supported(g, n):
+        v, part = ge.engram_wkv_gate_partials(g, wl.table, wl.scales, hid, wl.w, xf, wl.q, wl.k,
+                                              err=err_b)
+        out_b = ge.engram_gate_from_partials(g, xf, v, part, mask=mask.reshape(-1), gate=gate_b)
+    else:
+        if n <= 256 or n >= 1024:
+            kv = ge.engram_wkv_gathered(g, wl.table, wl.scales, hid, wl.w, err=err_b)
+        else:
+            kv = ge.engram_wkv(g, ge.engram_gather(g, wl.table, wl.scales, hid, err=err_b), wl.w)
+        out_b = ge.engram_gate_add(g, xf, kv, wl.q, wl.k, mask=mask.reshape(-1), gate=gate_b)
+    torch.cuda.synchronize()
+    bits_err = int(err_a.item())
+    assert bits_err == int(err_b.item())
+    assert bits_err & ge.ERRBIT_TOKEN and bits_err & ge.ERRBIT_HASH and bits_err & ge.ERRBIT_ROW
+    assert torch.equal(state_a, state_b)
+    assert torch.equal(out_a.view(torch.int16).reshape(-1), out_b.view(torch.int16).reshape(-1))
+    assert torch.equal(gate_a.reshape(-1), gate_b.reshape(-1))
