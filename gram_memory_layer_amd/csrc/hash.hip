@@ -1,23 +1,40 @@
 // Stage 1: the n-gram hash ("Module engram" docs, stage 1 and NgramHashState).
 //
-// One thread per (sequence, position, column): consecutive threads write
-// consecutive int32 hash ids, so the output is fully coalesced; the few
-// token-id and token_map reads per thread are shared through L1/L2 by the
-// n_cols threads of a position.  Arithmetic is unsigned 64-bit: the wrapping
-// multiply is built from 32-bit pieces by the compiler, the modulus is the
-// exact 64-bit unsigned remainder.
+// Arithmetic is unsigned 64-bit: the wrapping multiply is built from 32-bit
+// pieces by the compiler, the modulus is the exact 64-bit unsigned remainder.
+//
+// One kernel hashes and updates the carried state.  Only the first
+// n_state = max_ngram_size-1 positions of a sequence read the state, so the
+// work is split in two kinds of workgroups:
+//  * body workgroups take every (position, column) item at t >= n_state, one
+//    thread each, laid out so that the output stores are coalesced; they
+//    never touch the state;
+//  * head workgroups each own a few whole sequences: they hash those
+//    sequences' first min(T, n_state) positions (every column), then, after
+//    a workgroup barrier that orders all of this workgroup's state reads
+//    before any write, one thread per sequence writes the new state (the
+//    last n_state compressed ids).  No other workgroup reads those
+//    sequences' state, so the in-place update is race-free.
+// Without a state, every position reads the pad id and there are no head
+// workgroups.
+//
+// Two output forms: hash ids [M][n_cols] (column fastest), or the fused
+// projections' row offsets and scales [n_cols][m_pad] (row fastest, with
+// q*k beside them when asked).
 #include "internal.h"
 
 namespace engram {
 namespace {
+
+constexpr int kThreads = 256;
 
 // Compressed id at position p (relative to this call) of sequence b.
 // p < 0 reaches into the carried state (oldest first), or the pad id.
 __device__ __forceinline__ uint32_t compressed_at(int p, int b, int T, int n_state,
                                                   const int32_t* __restrict__ ids,
                                                   const int32_t* __restrict__ token_map,
-                                                  const int32_t* __restrict__ state, int vocab,
-                                                  int pad_id, uint32_t* bad) {
+                                                  const int32_t* state, int vocab, int pad_id,
+                                                  uint32_t* bad) {
     if (p < 0) {
         if (state == nullptr) return (uint32_t)pad_id;
         return (uint32_t)state[(int64_t)b * n_state + (n_state + p)];
@@ -30,111 +47,164 @@ __device__ __forceinline__ uint32_t compressed_at(int p, int b, int T, int n_sta
     return (uint32_t)token_map[tok];
 }
 
+struct HashArgs {
+    const int32_t* token_map;
+    const uint64_t* mult;
+    const uint64_t* prime;
+    const uint64_t* offset;
+    int32_t* state;  // [B][n_state] or null
+    const int32_t* ids;
+    int B, T, n_cols, n_heads, max_ngram, vocab, pad_id;
+    int64_t num_embeddings;
+    uint32_t* err;
+    // head workgroups: seq_per_head sequences each, after n_body body workgroups
+    int n_body, seq_per_head;
+    // hash-id form
+    int32_t* hash_ids;
+    // offsets-and-scales form
+    const uint8_t* scales;
+    int64_t m_pad;
+    uint32_t* aoff;
+    float2* scl;
+    const uint16_t* q;
+    const uint16_t* k;
+    float* wqk;
+    int nqk;
+};
+
 // Hash id of column col at position t of sequence b (the unsigned 64-bit
 // mix, reduced modulo the column's prime and moved by its offset); sets
 // ENGRAM_ERRBIT_HASH and gives -1 when that lands outside the table.
-__device__ __forceinline__ int32_t hash_at(int b, int t, int col, int T, int n_heads,
-                                           int max_ngram, const int32_t* __restrict__ ids,
-                                           const int32_t* __restrict__ token_map,
-                                           const uint64_t* __restrict__ mult,
-                                           const uint64_t* __restrict__ prime,
-                                           const uint64_t* __restrict__ offset,
-                                           const int32_t* __restrict__ state, int vocab,
-                                           int pad_id, int64_t num_embeddings, uint32_t* bad) {
-    const int n = 2 + col / n_heads;
-    const int n_state = max_ngram - 1;
+__device__ __forceinline__ int32_t hash_at(const HashArgs& a, int b, int t, int col,
+                                           uint32_t* bad) {
+    const int n = 2 + col / a.n_heads;
+    const int n_state = a.max_ngram - 1;
     uint64_t mix = 0;
     for (int k = 0; k < n; ++k) {
-        uint32_t c = compressed_at(t - k, b, T, n_state, ids, token_map, state, vocab, pad_id, bad);
-        mix ^= (uint64_t)c * mult[(int64_t)col * max_ngram + k];
+        uint32_t c = compressed_at(t - k, b, a.T, n_state, a.ids, a.token_map, a.state, a.vocab,
+                                   a.pad_id, bad);
+        mix ^= (uint64_t)c * a.mult[(int64_t)col * a.max_ngram + k];
     }
-    const uint64_t h = mix % prime[col] + offset[col];
-    if (h < (uint64_t)num_embeddings) return (int32_t)h;
+    const uint64_t h = mix % a.prime[col] + a.offset[col];
+    if (h < (uint64_t)a.num_embeddings) return (int32_t)h;
     *bad |= ENGRAM_ERRBIT_HASH;
     return -1;
 }
 
-__global__ void __launch_bounds__(256) hash_kernel(
-    const int32_t* __restrict__ token_map, const uint64_t* __restrict__ mult,
-    const uint64_t* __restrict__ prime, const uint64_t* __restrict__ offset,
-    const int32_t* __restrict__ state, const int32_t* __restrict__ ids, int B, int T,
-    int n_cols, int n_heads, int max_ngram, int vocab, int pad_id, int64_t num_embeddings,
-    int32_t* __restrict__ hash_ids, uint32_t* __restrict__ err) {
-    const int64_t total = (int64_t)B * T * n_cols;
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= total) return;
-    const int col = (int)(i % n_cols);
-    const int64_t bt = i / n_cols;
-    const int b = (int)(bt / T);
-    const int t = (int)(bt % T);
-    uint32_t bad = 0;
-    hash_ids[i] = hash_at(b, t, col, T, n_heads, max_ngram, ids, token_map, mult, prime, offset,
-                          state, vocab, pad_id, num_embeddings, &bad);
-    if (bad && err) atomicOr(err, bad);
-}
-
-// The hash, written straight in the form the fused projections read: one
-// thread per (column c, padded row m), m fastest, so the offset and scale
-// stores are coalesced.  Row m = b*T + t; rows past B*T are padding.  A hash
-// outside the table also counts as a bad row, as it does when the ids pass
-// through memory.  When wqk is given, q*k in fp32 as well.
-__global__ void __launch_bounds__(256) hash_prep_kernel(
-    const int32_t* __restrict__ token_map, const uint64_t* __restrict__ mult,
-    const uint64_t* __restrict__ prime, const uint64_t* __restrict__ offset,
-    const int32_t* __restrict__ state, const int32_t* __restrict__ ids, int B, int T,
-    int n_cols, int n_heads, int max_ngram, int vocab, int pad_id, int64_t num_embeddings,
-    const uint8_t* __restrict__ scales, int64_t m_pad, uint32_t* __restrict__ aoff,
-    float2* __restrict__ scl, uint32_t* __restrict__ err, const uint16_t* __restrict__ q,
-    const uint16_t* __restrict__ k, float* __restrict__ wqk, int nqk) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (wqk)
-        for (int64_t j = i; j < nqk; j += (int64_t)gridDim.x * blockDim.x)
-            wqk[j] = __uint_as_float((uint32_t)q[j] << 16) * __uint_as_float((uint32_t)k[j] << 16);
-    if (i >= (int64_t)n_cols * m_pad) return;
-    const int col = (int)(i / m_pad);
-    const int64_t m = i - (int64_t)col * m_pad;
+// Store the result of item (row m, column col) in the output form.  In the
+// offsets-and-scales form a hash outside the table is also a bad row, as it
+// is when the ids pass through memory to the projection.
+template <bool PREP>
+__device__ __forceinline__ void emit(const HashArgs& a, int64_t m, int col, int32_t id,
+                                     uint32_t* bad) {
+    if (!PREP) {
+        a.hash_ids[m * a.n_cols + col] = id;
+        return;
+    }
     uint32_t off = kBadRowOffset;
     float2 sc = make_float2(0.0f, 0.0f);
+    if (id >= 0) {
+        off = (uint32_t)id * 64u;
+        sc = make_float2(e8m0_scale(a.scales[2 * (int64_t)id]),
+                         e8m0_scale(a.scales[2 * (int64_t)id + 1]));
+    } else {
+        *bad |= ENGRAM_ERRBIT_ROW;
+    }
+    const int64_t i = (int64_t)col * a.m_pad + m;
+    a.aoff[i] = off;
+    a.scl[i] = sc;
+}
+
+template <bool PREP>
+__global__ void __launch_bounds__(kThreads) hash_kernel(HashArgs a) {
+    const int n_state = a.max_ngram - 1;
+    const int64_t M = (int64_t)a.B * a.T;
+    // with a state, positions t < n_state belong to the head workgroups
+    const int body_from = a.state ? n_state : 0;
     uint32_t bad = 0;
-    if (m < (int64_t)B * T) {
-        const int b = (int)(m / T);
-        const int t = (int)(m - (int64_t)b * T);
-        const int32_t id = hash_at(b, t, col, T, n_heads, max_ngram, ids, token_map, mult, prime,
-                                   offset, state, vocab, pad_id, num_embeddings, &bad);
-        if (id >= 0) {
-            off = (uint32_t)id * 64u;
-            sc = make_float2(e8m0_scale(scales[2 * (int64_t)id]),
-                             e8m0_scale(scales[2 * (int64_t)id + 1]));
-        } else {
-            bad |= ENGRAM_ERRBIT_ROW;
+    if ((int)blockIdx.x < a.n_body) {
+        const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+        if (PREP && a.wqk)
+            for (int64_t j = i; j < a.nqk; j += (int64_t)a.n_body * kThreads)
+                a.wqk[j] = __uint_as_float((uint32_t)a.q[j] << 16) *
+                           __uint_as_float((uint32_t)a.k[j] << 16);
+        int64_t m;
+        int col;
+        if (PREP) {  // rows fastest, padded rows included
+            if (i >= (int64_t)a.n_cols * a.m_pad) return;
+            col = (int)(i / a.m_pad);
+            m = i - (int64_t)col * a.m_pad;
+            if (m >= M) {
+                a.aoff[i] = kBadRowOffset;
+                a.scl[i] = make_float2(0.0f, 0.0f);
+                return;
+            }
+        } else {  // columns fastest
+            if (i >= M * a.n_cols) return;
+            col = (int)(i % a.n_cols);
+            m = i / a.n_cols;
+        }
+        const int b = (int)(m / a.T);
+        const int t = (int)(m - (int64_t)b * a.T);
+        if (t < body_from) return;
+        const int32_t id = hash_at(a, b, t, col, &bad);
+        emit<PREP>(a, m, col, id, &bad);
+    } else {
+        const int b0 = ((int)blockIdx.x - a.n_body) * a.seq_per_head;
+        const int nb = min(a.seq_per_head, a.B - b0);
+        const int hh = min(a.T, n_state);
+        const int items = nb * hh * a.n_cols;
+        for (int j = threadIdx.x; j < items; j += kThreads) {
+            const int col = j % a.n_cols;
+            const int r = j / a.n_cols;
+            const int b = b0 + r / hh;
+            const int t = r % hh;
+            const int32_t id = hash_at(a, b, t, col, &bad);
+            emit<PREP>(a, (int64_t)b * a.T + t, col, id, &bad);
+        }
+        // every state read of these sequences is above this barrier
+        __syncthreads();
+        if ((int)threadIdx.x < nb) {
+            const int b = b0 + threadIdx.x;
+            uint32_t v[16];
+            uint32_t ignored = 0;  // bad tokens were flagged by the hash itself
+            for (int j = 0; j < n_state; ++j)
+                v[j] = compressed_at(a.T - n_state + j, b, a.T, n_state, a.ids, a.token_map,
+                                     a.state, a.vocab, a.pad_id, &ignored);
+            for (int j = 0; j < n_state; ++j) a.state[(int64_t)b * n_state + j] = (int32_t)v[j];
         }
     }
-    aoff[i] = off;
-    scl[i] = sc;
-    if (bad && err) atomicOr(err, bad);
+    if (bad && a.err) atomicOr(a.err, bad);
 }
 
-// New state = the last n_state compressed ids after this call's T positions.
-// One thread per sequence reads everything it needs before writing, so the
-// in-place shift is race-free.
-__global__ void __launch_bounds__(64) state_kernel(const int32_t* __restrict__ token_map,
-                                                   const int32_t* __restrict__ ids, int B, int T,
-                                                   int n_state, int vocab, int pad_id,
-                                                   int32_t* state) {
-    const int b = blockIdx.x * blockDim.x + threadIdx.x;
-    if (b >= B) return;
-    uint32_t v[16];
-    uint32_t bad = 0;
-    for (int j = 0; j < n_state; ++j)
-        v[j] = compressed_at(T - n_state + j, b, T, n_state, ids, token_map, state, vocab,
-                             pad_id, &bad);
-    for (int j = 0; j < n_state; ++j) state[(int64_t)b * n_state + j] = (int32_t)v[j];
+HashArgs base_args(const Geom& g, const engram_hash_tables& t, int32_t* state, const int32_t* ids,
+                   int B, int T, uint32_t* err) {
+    HashArgs a{};
+    a.token_map = t.token_map;
+    a.mult = t.mult;
+    a.prime = t.prime;
+    a.offset = t.offset;
+    a.state = state;
+    a.ids = ids;
+    a.B = B;
+    a.T = T;
+    a.n_cols = g.n_cols;
+    a.n_heads = g.n_heads;
+    a.max_ngram = g.max_ngram;
+    a.vocab = g.vocab;
+    a.pad_id = g.pad_id;
+    a.num_embeddings = g.num_embeddings;
+    a.err = err;
+    return a;
 }
 
-void launch_state(const Geom& g, const engram_hash_tables& t, int32_t* state, const int32_t* ids,
-                  int B, int T, hipStream_t s) {
-    state_kernel<<<dim3((B + 63) / 64), dim3(64), 0, s>>>(t.token_map, ids, B, T, g.max_ngram - 1,
-                                                          g.vocab, g.pad_id, state);
+// Head workgroups: a few sequences each (up to one pass of the workgroup
+// over their head items), so that decode-sized calls spread over several CUs.
+int head_blocks(const Geom& g, int B, int T, int* seq_per_head) {
+    const int hh = std::min(T, g.max_ngram - 1);
+    const int per_seq = hh * g.n_cols;
+    *seq_per_head = std::max(1, std::min(4, kThreads / std::max(per_seq, 1)));
+    return (B + *seq_per_head - 1) / *seq_per_head;
 }
 
 }  // namespace
@@ -146,14 +216,19 @@ hipError_t launch_hash_prep(const Geom& g, const engram_hash_tables& t, int32_t*
     const int64_t M = (int64_t)B * T;
     if (M == 0) return hipSuccess;
     const GatheredScratch gs = gathered_scratch(g, M, scratch);
+    HashArgs a = base_args(g, t, state, ids, B, T, err);
+    a.scales = scales;
+    a.m_pad = gs.m_pad;
+    a.aoff = gs.aoff;
+    a.scl = gs.scl;
+    a.q = q;
+    a.k = k;
+    a.wqk = q ? gs.wqk : nullptr;
+    a.nqk = g.hc * g.dim;
     const int64_t total = (int64_t)g.n_cols * gs.m_pad;
-    hash_prep_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s>>>(
-        t.token_map, t.mult, t.prime, t.offset, state, ids, B, T, g.n_cols, g.n_heads,
-        g.max_ngram, g.vocab, g.pad_id, g.num_embeddings, scales, gs.m_pad, gs.aoff, gs.scl, err,
-        q, k, q ? gs.wqk : nullptr, g.hc * g.dim);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || state == nullptr) return e;
-    launch_state(g, t, state, ids, B, T, s);
+    a.n_body = (int)((total + kThreads - 1) / kThreads);
+    const int heads = state ? head_blocks(g, B, T, &a.seq_per_head) : 0;
+    hash_kernel<true><<<dim3((unsigned)(a.n_body + heads)), dim3(kThreads), 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -162,14 +237,11 @@ hipError_t launch_hash(const Geom& g, const engram_hash_tables& t, int32_t* stat
                        hipStream_t s) {
     const int64_t total = (int64_t)B * T * g.n_cols;
     if (total == 0) return hipSuccess;
-    const int threads = 256;
-    const int64_t blocks = (total + threads - 1) / threads;
-    hash_kernel<<<dim3((unsigned)blocks), dim3(threads), 0, s>>>(
-        t.token_map, t.mult, t.prime, t.offset, state, ids, B, T, g.n_cols, g.n_heads,
-        g.max_ngram, g.vocab, g.pad_id, g.num_embeddings, hash_ids, err);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || state == nullptr) return e;
-    launch_state(g, t, state, ids, B, T, s);
+    HashArgs a = base_args(g, t, state, ids, B, T, err);
+    a.hash_ids = hash_ids;
+    a.n_body = (int)((total + kThreads - 1) / kThreads);
+    const int heads = state ? head_blocks(g, B, T, &a.seq_per_head) : 0;
+    hash_kernel<false><<<dim3((unsigned)(a.n_body + heads)), dim3(kThreads), 0, s>>>(a);
     return hipGetLastError();
 }
 

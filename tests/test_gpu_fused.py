@@ -248,7 +248,7 @@ def test_gate_from_partials_against_oracle(ge, dev, gp_case):
 # gather + projection in between, the 256-wide fused tiles, and the fully
 # fused path with the gate's sums in the projection.
 FWD_CASES = [((256, 3, 3, 2), 1, 37), ((256, 3, 3, 2), 3, 100), ((256, 3, 3, 2), 1, 1100),
-             ((2048, 4, 3, 3), 1, 4096)]
+             ((2048, 4, 3, 3), 1, 4096), ((256, 3, 3, 2), 5, 1), ((256, 3, 5, 2), 3, 2)]
 
 
 @pytest.mark.parametrize("shape,B,T", FWD_CASES)
@@ -267,7 +267,7 @@ def test_forward_equals_stage_calls(ge, dev, shape, B, T):
               for k2 in ("token_map", "mult", "prime", "offset")}
     ids_np = synth.token_ids(cfg, B, T, name="fs")
     ids_np[0, min(5, T - 1)] = cfg.vocab + 7
-    ids_np[-1, T // 2] = -3
+    ids_np[-1, T // 2] = -3                           # (the same position when T = 1, B = 1)
     ids = torch.from_numpy(ids_np).to(dev)
     x = synth.activations(cfg, n, dev, name="fsx").reshape(B, T, hc, dim)
     mask = torch.from_numpy(synth.token_ids(cfg, B, T, name="fsm") % 4 != 0).to(dev)

@@ -67,6 +67,38 @@ def test_hash_state_carries_across_calls(ge, dev, tiny):
         assert np.array_equal(state.cpu().numpy(), tiny.t["token_map"][ids[:, -2:]])
 
 
+# The state is read only by a sequence's first max_ngram_size-1 positions,
+# which the hash kernel gives to workgroups that own whole sequences and
+# rewrite the state after they have read it.  Chunks shorter than the state
+# (the new state then keeps old entries), a sequence count that does not
+# fill the last such workgroup, and more head items per sequence than one
+# workgroup pass (n_cols 300).
+@pytest.mark.parametrize("mx,nh,B,chunks", [(5, 2, 7, (1, 3, 2, 4, 1, 9, 5)),
+                                            (3, 150, 5, (1, 2, 7, 1)),
+                                            (2, 1, 9, (1, 1, 3, 1))])
+def test_hash_state_split_geometries(ge, dev, mx, nh, B, chunks):
+    import dataclasses
+    cfg = dataclasses.replace(synth.config("tiny"), max_ngram_size=mx, n_heads=nh,
+                              prime_limit=100003)
+    say("hash split geometry", mx, nh, B, chunks)
+    wl = Workload(ge, cfg, dev, with_table=False, with_weights=False)
+    T = sum(chunks)
+    ids = synth.token_ids(cfg, B, T, name="splitg")
+    ref = oracle.hash_ids(wl.t, wl.geom, oracle.HashState(B, T + 4), ids)
+    state = torch.full((B, mx - 1), cfg.pad_id, dtype=torch.int32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    parts, s0 = [], 0
+    for c in chunks:
+        parts.append(ge.engram_hash(wl.g, wl.tables, torch.from_numpy(ids[:, s0:s0 + c].copy()).to(dev),
+                                    state=state, err=err))
+        s0 += c
+    got = torch.cat(parts, dim=1).cpu().numpy()
+    assert np.array_equal(got, ref)
+    assert int(err.item()) == 0
+    # the state holds the last n-1 compressed ids
+    assert np.array_equal(state.cpu().numpy(), wl.t["token_map"][ids[:, T - (mx - 1):]])
+
+
 def test_hash_bad_token_flags_and_stays_in_range(ge, dev, tiny):
     say("hash bad token")
     ids = synth.token_ids(tiny.cfg, 1, 16, name="bad")
