@@ -48,33 +48,39 @@ __device__ __forceinline__ float wave_sum(float v) {
 // PART: the key-side sums come as per-128-column partials from the
 // projection's epilogue (kv then points at the value [n_tok, dim] alone, q and
 // kw are unused); only S_hh is reduced here.
-template <int HC, int NCH, bool PART>
+// SPLIT: one workgroup per (token, stream), stream = blockIdx.y, for batches
+// too small to fill the machine with one workgroup per token.  Each stream's
+// sums are formed by the same threads in the same order either way, so the
+// results are identical.
+template <int HC, int NCH, bool PART, bool SPLIT = false>
 __global__ void __launch_bounds__(1024) gate_kernel(
     const uint16_t* x, const uint16_t* __restrict__ kv,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kw,
     const float2* __restrict__ part, const uint8_t* __restrict__ mask, int dim, float eps,
     float inv_sqrt_dim, uint16_t* out, float* __restrict__ gate) {
 #pragma clang fp contract(off)
-    constexpr int NS = PART ? HC : 3 * HC;
+    constexpr int HS = SPLIT ? 1 : HC;  // streams of this workgroup
+    constexpr int NS = PART ? HS : 3 * HS;
     __shared__ float red[16][NS];
-    __shared__ float gsh[HC];
+    __shared__ float gsh[HS];
 
     const int64_t tok = blockIdx.x;
+    const int s0 = SPLIT ? (int)blockIdx.y : 0;  // first stream of this workgroup
     const int tid = threadIdx.x;
     const int nthr = blockDim.x;
     const int d8 = dim / 8;
     const int64_t row = PART ? (int64_t)dim : (int64_t)dim * (HC + 1);
     const int64_t voff = PART ? 0 : (int64_t)HC * dim;  // value within the kv row
-    const uint16_t* xt = x + tok * HC * dim;
+    const uint16_t* xt = x + (tok * HC + s0) * dim;
     const uint16_t* kvt = kv + tok * row;
-    uint16_t* ot = out + tok * HC * dim;
+    uint16_t* ot = out + (tok * HC + s0) * dim;
     const bool live = (mask == nullptr) || (mask[tok] != 0);
 
     // KEEP: x and the value stay in registers from the loads to the output
     // pass; for wide geometries (HC * NCH > 8) they are re-read instead.
-    constexpr bool KEEP = HC * NCH <= 8;
+    constexpr bool KEEP = HS * NCH <= 8;
     constexpr int KC = KEEP ? NCH : 1;
-    uint4 xr[HC][KC];
+    uint4 xr[HS][KC];
     if (!live) {
         // masked position: the gate is 0 and x passes through unchanged
 #pragma unroll
@@ -82,22 +88,23 @@ __global__ void __launch_bounds__(1024) gate_kernel(
             const int c = tid + i * nthr;
             if (c < d8)
 #pragma unroll
-                for (int s = 0; s < HC; ++s) {
+                for (int s = 0; s < HS; ++s) {
                     st_nt(ot + (int64_t)s * dim + c * 8,
                           *reinterpret_cast<const uint4*>(xt + (int64_t)s * dim + c * 8));
                 }
         }
-        if (gate && tid < HC) gate[tok * HC + tid] = 0.0f;
+        if (gate && tid < HS) gate[tok * HC + s0 + tid] = 0.0f;
         return;
     }
 
     // PART: the token's HC * dim/128 partial pairs are fetched first, one per
     // thread, into LDS, so their latency overlaps the x loads; they are
     // summed in order after the block reduction
-    __shared__ float2 psh[PART ? HC * 256 : 1];
+    __shared__ float2 psh[PART ? HS * 256 : 1];
     if constexpr (PART) {
-        const int np = HC * (dim >> 7);  // dim <= 32768: at most HC * 256 pairs
-        for (int t = tid; t < np; t += nthr) psh[t] = part[tok * np + t];
+        const int np = HS * (dim >> 7);  // dim <= 32768: at most HS * 256 pairs
+        const float2* pt = part + (tok * HC + s0) * (dim >> 7);
+        for (int t = tid; t < np; t += nthr) psh[t] = pt[t];
     }
 
     float acc[NS];
@@ -110,7 +117,7 @@ __global__ void __launch_bounds__(1024) gate_kernel(
         if (c < d8) {
             if (KEEP) vr[i < KC ? i : 0] = *reinterpret_cast<const uint4*>(kvt + voff + c * 8);
 #pragma unroll
-            for (int s = 0; s < HC; ++s) {
+            for (int s = 0; s < HS; ++s) {
                 const uint4 h = *reinterpret_cast<const uint4*>(xt + (int64_t)s * dim + c * 8);
                 if (KEEP) xr[s][i < KC ? i : 0] = h;
                 if constexpr (PART) {
@@ -122,9 +129,10 @@ __global__ void __launch_bounds__(1024) gate_kernel(
                         acc[s] += h1 * h1;
                     }
                 } else {
-                    const uint4 key = *reinterpret_cast<const uint4*>(kvt + (int64_t)s * dim + c * 8);
-                    const uint4 qq = *reinterpret_cast<const uint4*>(q + (int64_t)s * dim + c * 8);
-                    const uint4 kk = *reinterpret_cast<const uint4*>(kw + (int64_t)s * dim + c * 8);
+                    const int64_t so = (int64_t)(s0 + s) * dim + c * 8;
+                    const uint4 key = *reinterpret_cast<const uint4*>(kvt + so);
+                    const uint4 qq = *reinterpret_cast<const uint4*>(q + so);
+                    const uint4 kk = *reinterpret_cast<const uint4*>(kw + so);
                     const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
                     const uint32_t kyw[4] = {key.x, key.y, key.z, key.w};
                     const uint32_t qw[4] = {qq.x, qq.y, qq.z, qq.w};
@@ -137,12 +145,12 @@ __global__ void __launch_bounds__(1024) gate_kernel(
                         const float w1 = hi_f(qw[e]) * hi_f(kw4[e]);
                         acc[s] += h0 * h0;
                         acc[s] += h1 * h1;
-                        acc[HC + s] += k0 * k0;
-                        acc[HC + s] += k1 * k1;
+                        acc[HS + s] += k0 * k0;
+                        acc[HS + s] += k1 * k1;
                         const float p0 = (h0 * w0) * k0;
                         const float p1 = (h1 * w1) * k1;
-                        acc[2 * HC + s] += p0;
-                        acc[2 * HC + s] += p1;
+                        acc[2 * HS + s] += p0;
+                        acc[2 * HS + s] += p1;
                     }
                 }
             }
@@ -157,13 +165,13 @@ __global__ void __launch_bounds__(1024) gate_kernel(
         if (lane == 0) red[wave][j] = v;
     }
     __syncthreads();
-    if (tid < HC) {
+    if (tid < HS) {
         float shh = 0.f, skk = 0.f, shwk = 0.f;
         for (int w = 0; w < nwaves; ++w) {
             shh += red[w][tid];
             if constexpr (!PART) {
-                skk += red[w][HC + tid];
-                shwk += red[w][2 * HC + tid];
+                skk += red[w][HS + tid];
+                shwk += red[w][2 * HS + tid];
             }
         }
         if constexpr (PART) {
@@ -181,13 +189,13 @@ __global__ void __launch_bounds__(1024) gate_kernel(
         const float sg = copysignf(sqrtf(mag), a);
         const float g = 1.0f / (1.0f + expf(-sg));
         gsh[tid] = g;
-        if (gate) gate[tok * HC + tid] = g;
+        if (gate) gate[tok * HC + s0 + tid] = g;
     }
     __syncthreads();
 
-    float g[HC];
+    float g[HS];
 #pragma unroll
-    for (int s = 0; s < HC; ++s) g[s] = gsh[s];
+    for (int s = 0; s < HS; ++s) g[s] = gsh[s];
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
         const int c = tid + i * nthr;
@@ -196,7 +204,7 @@ __global__ void __launch_bounds__(1024) gate_kernel(
                                   : *reinterpret_cast<const uint4*>(kvt + voff + c * 8);
             const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
-            for (int s = 0; s < HC; ++s) {
+            for (int s = 0; s < HS; ++s) {
                 const uint4 hh = KEEP ? xr[s][i < KC ? i : 0]
                                       : *reinterpret_cast<const uint4*>(xt + (int64_t)s * dim + c * 8);
                 const uint32_t hw[4] = {hh.x, hh.y, hh.z, hh.w};
@@ -225,11 +233,18 @@ hipError_t run_hc(const Geom& g, const uint16_t* x, const uint16_t* kv, const ui
     int threads = (d8 + nch - 1) / nch;
     threads = (threads + 63) / 64 * 64;
     const float inv_sqrt_dim = (float)(1.0 / sqrt((double)g.dim));
-    const dim3 grid((unsigned)n_tok), block(threads);
+    // fewer tokens than about four workgroups per compute unit: one
+    // workgroup per (token, stream) instead of one per token
+    const bool split = HC > 1 && n_tok < 4 * (int64_t)cu_count();
+    const dim3 grid((unsigned)n_tok, split ? HC : 1), block(threads);
 #define ENGRAM_GATE_CASE(N)                                                                  \
     case N:                                                                                  \
-        gate_kernel<HC, N, PART><<<grid, block, 0, s>>>(x, kv, q, k, part, mask, g.dim,      \
-                                                        g.eps, inv_sqrt_dim, out, gate);     \
+        if (split)                                                                           \
+            gate_kernel<HC, N, PART, true><<<grid, block, 0, s>>>(                           \
+                x, kv, q, k, part, mask, g.dim, g.eps, inv_sqrt_dim, out, gate);             \
+        else                                                                                 \
+            gate_kernel<HC, N, PART, false><<<grid, block, 0, s>>>(                          \
+                x, kv, q, k, part, mask, g.dim, g.eps, inv_sqrt_dim, out, gate);             \
         break;
     switch (nch) {
         ENGRAM_GATE_CASE(1)

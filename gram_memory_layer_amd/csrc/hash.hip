@@ -154,6 +154,19 @@ __global__ void __launch_bounds__(kThreads) hash_kernel(HashArgs a) {
         const int nb = min(a.seq_per_head, a.B - b0);
         const int hh = min(a.T, n_state);
         const int items = nb * hh * a.n_cols;
+        // the new state, read first so that its loads overlap the hash work
+        // (n_state <= 15; the fully unrolled loops keep v in registers)
+        uint32_t v[16];
+        const bool writer = (int)threadIdx.x < nb;
+        if (writer) {
+            const int b = b0 + threadIdx.x;
+            uint32_t ignored = 0;  // bad tokens are flagged by the hash itself
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                if (j < n_state)
+                    v[j] = compressed_at(a.T - n_state + j, b, a.T, n_state, a.ids, a.token_map,
+                                         a.state, a.vocab, a.pad_id, &ignored);
+        }
         for (int j = threadIdx.x; j < items; j += kThreads) {
             const int col = j % a.n_cols;
             const int r = j / a.n_cols;
@@ -164,14 +177,11 @@ __global__ void __launch_bounds__(kThreads) hash_kernel(HashArgs a) {
         }
         // every state read of these sequences is above this barrier
         __syncthreads();
-        if ((int)threadIdx.x < nb) {
+        if (writer) {
             const int b = b0 + threadIdx.x;
-            uint32_t v[16];
-            uint32_t ignored = 0;  // bad tokens were flagged by the hash itself
-            for (int j = 0; j < n_state; ++j)
-                v[j] = compressed_at(a.T - n_state + j, b, a.T, n_state, a.ids, a.token_map,
-                                     a.state, a.vocab, a.pad_id, &ignored);
-            for (int j = 0; j < n_state; ++j) a.state[(int64_t)b * n_state + j] = (int32_t)v[j];
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                if (j < n_state) a.state[(int64_t)b * n_state + j] = (int32_t)v[j];
         }
     }
     if (bad && a.err) atomicOr(a.err, bad);

@@ -279,6 +279,39 @@ def test_gate_full_width_stress_recipe(ge, dev):
     assert np.all(np.abs(gv - g0) <= np.spacing(g0)), gv[:4]
 
 
+def test_gate_small_batches_equal_large(ge, dev):
+    # batches under four tokens per compute unit run one workgroup per
+    # (token, stream) instead of one per token: the same sums in the same
+    # order, so both layouts must agree bit for bit (both gate forms)
+    cfg = synth.config("gate_stress")
+    t = synth.hash_tables(cfg)
+    g = geometry(ge, cfg, t["num_embeddings"])
+    say("gate small vs large batch")
+    n_big, n_small = 1100, 64
+    x, kv, q, k, _ = _gate_inputs(cfg, n_big, dev, name="split")
+    x = x.reshape(n_big, cfg.hc_mult, cfg.dim)
+    mask = torch.from_numpy(synth.token_ids(cfg, 1, n_big, name="splitm")[0] % 5 != 0).to(dev)
+    gen = torch.Generator(device=dev).manual_seed(77)
+    nq = cfg.dim // 128
+    part = torch.randn((n_big, cfg.hc_mult, nq, 2), generator=gen, device=dev)
+    part[..., 0] = part[..., 0].abs() * 40.0
+    v = kv[:, cfg.hc_mult * cfg.dim:].contiguous()
+    for form in ("kv", "partials"):
+        outs, gates = [], []
+        for n in (n_big, n_small):
+            gate = torch.empty((n, cfg.hc_mult), dtype=torch.float32, device=dev)
+            if form == "kv":
+                o = ge.engram_gate_add(g, x[:n], kv[:n], q, k, mask=mask[:n], gate=gate)
+            else:
+                o = ge.engram_gate_from_partials(g, x[:n], v[:n], part[:n], mask=mask[:n],
+                                                 gate=gate)
+            outs.append(o)
+            gates.append(gate)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0][:n_small].view(torch.int16), outs[1].view(torch.int16)), form
+        assert torch.equal(gates[0][:n_small], gates[1]), form
+
+
 @pytest.mark.parametrize("hc,dim,n_tok", [(3, 16384, 6), (8, 32768, 3), (1, 8, 50), (2, 1000, 33)])
 def test_gate_other_geometries(ge, dev, hc, dim, n_tok):
     # streaming variant (x and value re-read), tiny dims, odd chunk counts
