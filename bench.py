@@ -43,9 +43,11 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run 3 plain device copies of exactly 1 GiB (a known-size kernel "
                         "against which HBM byte counters are scaled)")
-    p.add_argument("--workload", choices=("prefill", "decode"), default="prefill",
-                   help="prefill (the default and the headline line) or decode: 128 steps "
-                        "of 64 sequences after a 512-token prefill, replayed as one graph")
+    p.add_argument("--workload", choices=("prefill", "decode", "long_mixed"), default="prefill",
+                   help="prefill (the default and the headline line); decode: 128 steps "
+                        "of 64 sequences after a 512-token prefill, replayed as one graph; "
+                        "long_mixed: T=32768 with Zipf(1.1) ids and 30%% of positions masked "
+                        "in spans")
     p.add_argument("--summarize", nargs=3, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR"),
                    help="no GPU work: turn the CSV output of three rocprofv3 runs of this "
                         "script (--kernel-trace --stats; --pmc FETCH_SIZE; --pmc WRITE_SIZE, "
@@ -219,6 +221,9 @@ def main():
         sys.exit(2)
     if args.workload == "decode":
         decode(args)
+        return
+    if args.workload == "long_mixed":
+        long_mixed(args)
         return
     import numpy as np
     import torch
@@ -434,6 +439,99 @@ def decode(args):
                      "traffic": None},
         "eager_ms_per_step": round(eager * 1e3, 4),
         "projection_us": round(st_proj * 1e6, 2),
+        "wall_s": round(wall, 3),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def long_mixed(args):
+    """Long mixed prefill: B=1, T=32768, Zipf(1.1) token ids, 30% of the
+    positions masked in spans of 256..1024.  The forward projects only the
+    live positions (packed in order).  Also timed: the same work through the
+    dense stage calls (every position projected, then the masked gate), and
+    engram_wkv_gate_partials on the live positions alone, whose flops over
+    its call time give the roofline line."""
+    import numpy as np
+    import torch
+
+    import gram_memory_layer_amd as ge
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = synth.config("long_mixed")
+    t = synth.hash_tables(cfg)
+    g = ge.Geometry.make(cfg.dim, cfg.hc_mult, cfg.max_ngram_size, cfg.n_heads, cfg.head_dim,
+                         t["num_embeddings"], cfg.vocab, cfg.pad_id, cfg.norm_eps)
+    tables = {k: torch.from_numpy(t[k]).to(dev) for k in ("token_map", "mult", "prime", "offset")}
+    table, scales = synth.embedding_table(cfg, t["num_embeddings"], dev)
+    w = synth.wkv_weight(cfg, dev)
+    q, k = synth.qk_weights(cfg, dev)
+    B, T = cfg.B, cfg.T
+    n_tok = B * T
+    ids = torch.from_numpy(synth.token_ids(cfg, B, T)).to(dev)
+    x = synth.activations(cfg, n_tok, dev).reshape(B, T, cfg.hc_mult, cfg.dim)
+    mask_np = synth.token_mask(cfg, B, T)
+    mask = torch.from_numpy(mask_np).to(dev)
+    out = torch.empty_like(x)
+    layer = ge.EngramLayer(g, tables, table, scales, w, q, k)
+    ws = layer.workspace(n_tok)
+    stream = torch.cuda.current_stream(dev)
+    steps = max(args.steps // 5, 5)
+    warm = max(args.warmup // 5, 3)
+
+    def step():
+        ge.engram_forward(g, tables, table, scales, w, q, k, x, ids, mask=mask, out=out,
+                          workspace=ws)
+
+    for _ in range(warm):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    sec = time_launches(step, steps, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # the dense stage calls over the same inputs
+    xf = x.reshape(n_tok, cfg.hc_mult, cfg.dim)
+    outf = out.reshape(n_tok, cfg.hc_mult, cfg.dim)
+    hid = ge.engram_hash(g, tables, ids).reshape(n_tok, -1)
+    v, part = ge.engram_wkv_gate_partials(g, table, scales, hid, w, xf, q, k)
+    scratch = torch.empty(ge.engram_wkv_gathered_scratch_size(g, n_tok), dtype=torch.uint8,
+                          device=dev)
+
+    def dense():
+        ge.engram_hash(g, tables, ids, hash_ids=hid.reshape(B, T, -1))
+        ge.engram_wkv_gate_partials(g, table, scales, hid, w, xf, q, k, v=v, part=part,
+                                    scratch=scratch)
+        ge.engram_gate_from_partials(g, xf, v, part, mask=mask.reshape(-1), out=outf)
+
+    dense()
+    sec_dense = time_launches(dense, steps, stream)
+    # the projection over the live positions alone
+    live = torch.from_numpy(np.nonzero(mask_np.reshape(-1))[0]).to(dev)
+    n_live = int(live.numel())
+    hid_l = hid.index_select(0, live).contiguous()
+    x_l = xf.index_select(0, live).contiguous()
+    v_l, part_l = ge.engram_wkv_gate_partials(g, table, scales, hid_l, w, x_l, q, k)
+    sec_proj = time_launches(
+        lambda: ge.engram_wkv_gate_partials(g, table, scales, hid_l, w, x_l, q, k, v=v_l,
+                                            part=part_l), steps, stream)
+    achieved = 2 * g.K * g.N * n_live / sec_proj / 1e12
+    rec = {
+        "metric": "Engram long mixed prefill tokens/s @dim5120 hc4 (1 GPU), T=32768, 30% masked",
+        "value": round(n_tok / sec, 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warm, "ms_per_step": round(sec * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "Engram long mixed prefill, B=1 T=32768, Zipf(1.1) ids, 30% "
+                               "masked in spans of 256..1024, dim=5120 hc=4",
+                   "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
+        "roofline": {"kernel": "engram_wkv_gate_partials (live positions)", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "live_positions": n_live,
+        "dense_stage_calls_ms": round(sec_dense * 1e3, 4),
+        "live_projection_ms": round(sec_proj * 1e3, 4),
         "wall_s": round(wall, 3),
     }
     print(json.dumps(rec), flush=True)

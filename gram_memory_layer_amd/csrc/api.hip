@@ -203,8 +203,12 @@ size_t engram_forward_workspace_size(const engram_geometry* g, int64_t n_tok) {
     const Geom gg = engram::make_geom(*g);
     const size_t rows = (size_t)n_tok * gg.K * sizeof(uint16_t);
     const size_t scl = engram::gathered_scratch_bytes(gg, n_tok);
+    // + the live-row maps of the masked fully fused path
+    const size_t live = align256((size_t)n_tok * sizeof(int32_t)) +
+                        align256((size_t)engram::padded_rows(n_tok) * sizeof(int32_t)) + 256;
     return align256((size_t)n_tok * gg.n_cols * sizeof(int32_t)) +
-           align256(rows > scl ? rows : scl) + align256((size_t)n_tok * gg.N * sizeof(uint16_t));
+           align256(rows > scl ? rows : scl) + align256((size_t)n_tok * gg.N * sizeof(uint16_t)) +
+           live;
 }
 
 engram_status engram_forward(const engram_geometry* g, const engram_hash_tables* t,
@@ -238,6 +242,12 @@ engram_status engram_forward(const engram_geometry* g, const engram_hash_tables*
         ws += align256(rb > sb ? rb : sb);
     }
     uint16_t* kv = (uint16_t*)ws;
+    ws += align256((size_t)n_tok * gg.N * sizeof(uint16_t));
+    int32_t* live_idx = (int32_t*)ws;
+    ws += align256((size_t)n_tok * sizeof(int32_t));
+    int32_t* rowmap = (int32_t*)ws;
+    ws += align256((size_t)engram::padded_rows(n_tok) * sizeof(int32_t));
+    int* m_live = (int*)ws;
     hipStream_t s = (hipStream_t)stream;
     // the fused gather + projection where its layout applies: 256-wide tiles
     // for prefill-sized batches, 64-wide ones for decode-sized batches;
@@ -248,16 +258,28 @@ engram_status engram_forward(const engram_geometry* g, const engram_hash_tables*
         // fully fused: the hash writes the projection's row offsets and
         // scales directly; the projection reduces the key columns into the
         // gate's partial sums and stores only the value; kv's region holds both
+        // With a mask, only live positions are projected: they are packed
+        // in order into the first rows (v and part then hold compact rows).
         uint16_t* v = kv;
         float2* part = reinterpret_cast<float2*>(
             reinterpret_cast<char*>(kv) + align256((size_t)n_tok * gg.dim * sizeof(uint16_t)));
-        const engram::GatePartials gp{x, q, k, part, gg.dim, gg.hc};
-        hipError_t e = engram::launch_hash_prep(gg, *t, state, ids, B, T, scales, q, k, rows, err, s);
+        engram::GatePartials gp{x, q, k, part, gg.dim, gg.hc};
+        hipError_t e = hipSuccess;
+        if (mask) {
+            e = engram::launch_live_rows(mask, n_tok, engram::padded_rows(n_tok), live_idx, rowmap,
+                                         m_live, s);
+            gp.m_live = m_live;
+            gp.rowmap = rowmap;
+        }
+        if (e == hipSuccess)
+            e = engram::launch_hash_prep(gg, *t, state, ids, B, T, scales, q, k, rows, err, s,
+                                         mask ? live_idx : nullptr, mask ? m_live : nullptr);
         if (e == hipSuccess)
             e = engram::launch_wkv_gate_partials(gg, nullptr, table, scales, w, n_tok, gp, v, rows,
                                                  err, s, /*prepared=*/true);
         if (e == hipSuccess)
-            e = engram::launch_gate_from_partials(gg, x, v, part, mask, n_tok, out, gate, s);
+            e = engram::launch_gate_from_partials(gg, x, v, part, mask, n_tok, out, gate, s,
+                                                  mask ? live_idx : nullptr);
         return from_hip(e);
     }
     hipError_t e;

@@ -56,8 +56,9 @@ template <int HC, int NCH, bool PART, bool SPLIT = false>
 __global__ void __launch_bounds__(1024) gate_kernel(
     const uint16_t* x, const uint16_t* __restrict__ kv,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kw,
-    const float2* __restrict__ part, const uint8_t* __restrict__ mask, int dim, float eps,
-    float inv_sqrt_dim, uint16_t* out, float* __restrict__ gate) {
+    const float2* __restrict__ part, const uint8_t* __restrict__ mask,
+    const int32_t* __restrict__ live_idx, int dim, float eps, float inv_sqrt_dim, uint16_t* out,
+    float* __restrict__ gate) {
 #pragma clang fp contract(off)
     constexpr int HS = SPLIT ? 1 : HC;  // streams of this workgroup
     constexpr int NS = PART ? HS : 3 * HS;
@@ -72,9 +73,14 @@ __global__ void __launch_bounds__(1024) gate_kernel(
     const int64_t row = PART ? (int64_t)dim : (int64_t)dim * (HC + 1);
     const int64_t voff = PART ? 0 : (int64_t)HC * dim;  // value within the kv row
     const uint16_t* xt = x + (tok * HC + s0) * dim;
-    const uint16_t* kvt = kv + tok * row;
     uint16_t* ot = out + (tok * HC + s0) * dim;
+    // compacted rows (fully fused prefill under a mask): the value and the
+    // partial sums of a live position sit at its compact row (loaded
+    // alongside the mask byte, not after it)
+    const int32_t crow = (PART && live_idx) ? live_idx[tok] : 0;
     const bool live = (mask == nullptr) || (mask[tok] != 0);
+    const int64_t vrow = (PART && live_idx) ? (int64_t)crow : tok;
+    const uint16_t* kvt = kv + vrow * row;
 
     // KEEP: x and the value stay in registers from the loads to the output
     // pass; for wide geometries (HC * NCH > 8) they are re-read instead.
@@ -103,7 +109,7 @@ __global__ void __launch_bounds__(1024) gate_kernel(
     __shared__ float2 psh[PART ? HS * 256 : 1];
     if constexpr (PART) {
         const int np = HS * (dim >> 7);  // dim <= 32768: at most HS * 256 pairs
-        const float2* pt = part + (tok * HC + s0) * (dim >> 7);
+        const float2* pt = part + (vrow * HC + s0) * (dim >> 7);
         for (int t = tid; t < np; t += nthr) psh[t] = pt[t];
     }
 
@@ -223,8 +229,9 @@ __global__ void __launch_bounds__(1024) gate_kernel(
 
 template <int HC, bool PART>
 hipError_t run_hc(const Geom& g, const uint16_t* x, const uint16_t* kv, const uint16_t* q,
-                  const uint16_t* k, const float2* part, const uint8_t* mask, int64_t n_tok,
-                  uint16_t* out, float* gate, hipStream_t s) {
+                  const uint16_t* k, const float2* part, const uint8_t* mask,
+                  const int32_t* live_idx, int64_t n_tok, uint16_t* out, float* gate,
+                  hipStream_t s) {
     const int d8 = g.dim / 8;
     // one 16-byte chunk per thread and stream up to 1024 threads (640 at
     // dim 5120): measured faster than fewer threads holding more chunks
@@ -241,10 +248,10 @@ hipError_t run_hc(const Geom& g, const uint16_t* x, const uint16_t* kv, const ui
     case N:                                                                                  \
         if (split)                                                                           \
             gate_kernel<HC, N, PART, true><<<grid, block, 0, s>>>(                           \
-                x, kv, q, k, part, mask, g.dim, g.eps, inv_sqrt_dim, out, gate);             \
+                x, kv, q, k, part, mask, live_idx, g.dim, g.eps, inv_sqrt_dim, out, gate);   \
         else                                                                                 \
             gate_kernel<HC, N, PART, false><<<grid, block, 0, s>>>(                          \
-                x, kv, q, k, part, mask, g.dim, g.eps, inv_sqrt_dim, out, gate);             \
+                x, kv, q, k, part, mask, live_idx, g.dim, g.eps, inv_sqrt_dim, out, gate);   \
         break;
     switch (nch) {
         ENGRAM_GATE_CASE(1)
@@ -263,32 +270,33 @@ hipError_t launch_gate_add(const Geom& g, const uint16_t* x, const uint16_t* kv,
                            int64_t n_tok, uint16_t* out, float* gate, hipStream_t s) {
     if (n_tok == 0) return hipSuccess;
     switch (g.hc) {
-        case 1: return run_hc<1, false>(g, x, kv, q, k, nullptr, mask, n_tok, out, gate, s);
-        case 2: return run_hc<2, false>(g, x, kv, q, k, nullptr, mask, n_tok, out, gate, s);
-        case 3: return run_hc<3, false>(g, x, kv, q, k, nullptr, mask, n_tok, out, gate, s);
-        case 4: return run_hc<4, false>(g, x, kv, q, k, nullptr, mask, n_tok, out, gate, s);
-        case 5: return run_hc<5, false>(g, x, kv, q, k, nullptr, mask, n_tok, out, gate, s);
-        case 6: return run_hc<6, false>(g, x, kv, q, k, nullptr, mask, n_tok, out, gate, s);
-        case 7: return run_hc<7, false>(g, x, kv, q, k, nullptr, mask, n_tok, out, gate, s);
-        case 8: return run_hc<8, false>(g, x, kv, q, k, nullptr, mask, n_tok, out, gate, s);
+        case 1: return run_hc<1, false>(g, x, kv, q, k, nullptr, mask, nullptr, n_tok, out, gate, s);
+        case 2: return run_hc<2, false>(g, x, kv, q, k, nullptr, mask, nullptr, n_tok, out, gate, s);
+        case 3: return run_hc<3, false>(g, x, kv, q, k, nullptr, mask, nullptr, n_tok, out, gate, s);
+        case 4: return run_hc<4, false>(g, x, kv, q, k, nullptr, mask, nullptr, n_tok, out, gate, s);
+        case 5: return run_hc<5, false>(g, x, kv, q, k, nullptr, mask, nullptr, n_tok, out, gate, s);
+        case 6: return run_hc<6, false>(g, x, kv, q, k, nullptr, mask, nullptr, n_tok, out, gate, s);
+        case 7: return run_hc<7, false>(g, x, kv, q, k, nullptr, mask, nullptr, n_tok, out, gate, s);
+        case 8: return run_hc<8, false>(g, x, kv, q, k, nullptr, mask, nullptr, n_tok, out, gate, s);
         default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_gate_from_partials(const Geom& g, const uint16_t* x, const uint16_t* v,
                                      const float2* part, const uint8_t* mask, int64_t n_tok,
-                                     uint16_t* out, float* gate, hipStream_t s) {
+                                     uint16_t* out, float* gate, hipStream_t s,
+                                     const int32_t* live_idx) {
     if (n_tok == 0) return hipSuccess;
-    if (g.dim % 128 != 0) return hipErrorInvalidValue;
+    if (g.dim % 128 != 0 || (live_idx && !mask)) return hipErrorInvalidValue;
     switch (g.hc) {
-        case 1: return run_hc<1, true>(g, x, v, nullptr, nullptr, part, mask, n_tok, out, gate, s);
-        case 2: return run_hc<2, true>(g, x, v, nullptr, nullptr, part, mask, n_tok, out, gate, s);
-        case 3: return run_hc<3, true>(g, x, v, nullptr, nullptr, part, mask, n_tok, out, gate, s);
-        case 4: return run_hc<4, true>(g, x, v, nullptr, nullptr, part, mask, n_tok, out, gate, s);
-        case 5: return run_hc<5, true>(g, x, v, nullptr, nullptr, part, mask, n_tok, out, gate, s);
-        case 6: return run_hc<6, true>(g, x, v, nullptr, nullptr, part, mask, n_tok, out, gate, s);
-        case 7: return run_hc<7, true>(g, x, v, nullptr, nullptr, part, mask, n_tok, out, gate, s);
-        case 8: return run_hc<8, true>(g, x, v, nullptr, nullptr, part, mask, n_tok, out, gate, s);
+        case 1: return run_hc<1, true>(g, x, v, nullptr, nullptr, part, mask, live_idx, n_tok, out, gate, s);
+        case 2: return run_hc<2, true>(g, x, v, nullptr, nullptr, part, mask, live_idx, n_tok, out, gate, s);
+        case 3: return run_hc<3, true>(g, x, v, nullptr, nullptr, part, mask, live_idx, n_tok, out, gate, s);
+        case 4: return run_hc<4, true>(g, x, v, nullptr, nullptr, part, mask, live_idx, n_tok, out, gate, s);
+        case 5: return run_hc<5, true>(g, x, v, nullptr, nullptr, part, mask, live_idx, n_tok, out, gate, s);
+        case 6: return run_hc<6, true>(g, x, v, nullptr, nullptr, part, mask, live_idx, n_tok, out, gate, s);
+        case 7: return run_hc<7, true>(g, x, v, nullptr, nullptr, part, mask, live_idx, n_tok, out, gate, s);
+        case 8: return run_hc<8, true>(g, x, v, nullptr, nullptr, part, mask, live_idx, n_tok, out, gate, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -70,6 +70,9 @@ struct HashArgs {
     const uint16_t* k;
     float* wqk;
     int nqk;
+    // compacted rows (masked prefill): live positions go to row live_idx[m]
+    const int32_t* live_idx;
+    const int* m_live;
 };
 
 // Hash id of column col at position t of sequence b (the unsigned 64-bit
@@ -91,15 +94,21 @@ __device__ __forceinline__ int32_t hash_at(const HashArgs& a, int b, int t, int 
     return -1;
 }
 
-// Store the result of item (row m, column col) in the output form.  In the
-// offsets-and-scales form a hash outside the table is also a bad row, as it
-// is when the ids pass through memory to the projection.
+// Store the result of item (position m, column col) in the output form.  In
+// the offsets-and-scales form a hash outside the table is also a bad row, as
+// it is when the ids pass through memory to the projection; with compacted
+// rows a masked position is not placed (and its row never read).
 template <bool PREP>
 __device__ __forceinline__ void emit(const HashArgs& a, int64_t m, int col, int32_t id,
                                      uint32_t* bad) {
     if (!PREP) {
         a.hash_ids[m * a.n_cols + col] = id;
         return;
+    }
+    int64_t r = m;
+    if (a.live_idx && *a.m_live < a.B * (int64_t)a.T) {  // (all live: the identity)
+        r = a.live_idx[m];
+        if (r < 0) return;
     }
     uint32_t off = kBadRowOffset;
     float2 sc = make_float2(0.0f, 0.0f);
@@ -110,7 +119,7 @@ __device__ __forceinline__ void emit(const HashArgs& a, int64_t m, int col, int3
     } else {
         *bad |= ENGRAM_ERRBIT_ROW;
     }
-    const int64_t i = (int64_t)col * a.m_pad + m;
+    const int64_t i = (int64_t)col * a.m_pad + r;
     a.aoff[i] = off;
     a.scl[i] = sc;
 }
@@ -134,11 +143,13 @@ __global__ void __launch_bounds__(kThreads) hash_kernel(HashArgs a) {
             if (i >= (int64_t)a.n_cols * a.m_pad) return;
             col = (int)(i / a.m_pad);
             m = i - (int64_t)col * a.m_pad;
-            if (m >= M) {
+            // row m holds no position from the row count on (M, or the live
+            // count when compacted): a bad row
+            if (m >= (a.live_idx ? (int64_t)*a.m_live : M)) {
                 a.aoff[i] = kBadRowOffset;
                 a.scl[i] = make_float2(0.0f, 0.0f);
-                return;
             }
+            if (m >= M) return;
         } else {  // columns fastest
             if (i >= M * a.n_cols) return;
             col = (int)(i % a.n_cols);
@@ -222,11 +233,14 @@ int head_blocks(const Geom& g, int B, int T, int* seq_per_head) {
 hipError_t launch_hash_prep(const Geom& g, const engram_hash_tables& t, int32_t* state,
                             const int32_t* ids, int B, int T, const uint8_t* scales,
                             const uint16_t* q, const uint16_t* k, void* scratch, uint32_t* err,
-                            hipStream_t s) {
+                            hipStream_t s, const int32_t* live_idx, const int* m_live) {
     const int64_t M = (int64_t)B * T;
     if (M == 0) return hipSuccess;
+    if ((live_idx == nullptr) != (m_live == nullptr)) return hipErrorInvalidValue;
     const GatheredScratch gs = gathered_scratch(g, M, scratch);
     HashArgs a = base_args(g, t, state, ids, B, T, err);
+    a.live_idx = live_idx;
+    a.m_live = m_live;
     a.scales = scales;
     a.m_pad = gs.m_pad;
     a.aoff = gs.aoff;

@@ -57,7 +57,19 @@ struct GatePartials {
     float2* part;       // [M, hc, dim / 128] (sum key^2, sum (h*w)*key)
     int dim, hc;
     const float* wqk;   // [hc, dim] q*k in fp32 (filled by the launcher)
+    // Compacted rows (positions whose mask is False are left out): row r of
+    // the projection is position rowmap[r] of x; only the first *m_live rows
+    // hold positions, tiles past them are skipped.  Both null: dense.
+    const int* m_live = nullptr;
+    const int32_t* rowmap = nullptr;
 };
+
+// Compaction of the live (mask True) positions, in order: live_idx[m] = the
+// position's compact row (or -1 when masked), rowmap[r] = the position of
+// compact row r (M for r >= the live count, up to m_pad), *m_live = the
+// live count.  One workgroup.
+hipError_t launch_live_rows(const uint8_t* mask, int64_t M, int64_t m_pad, int32_t* live_idx,
+                            int32_t* rowmap, int* m_live, hipStream_t s);
 
 // Scratch of the fused projections: per (hash column c, padded row m) the
 // table byte offset of row hash_ids[m][c] (kBadRowOffset, past any table,
@@ -86,10 +98,14 @@ __device__ __forceinline__ float e8m0_scale(uint32_t c) {
 // themselves are not written): for every position and hash column, the row
 // offset and scales; q*k as well when q is given; the state updated as in
 // launch_hash.
+// With live_idx (from launch_live_rows), live positions go to their compact
+// rows and masked ones are hashed (their token and hash checks still flag)
+// but not placed; compact rows from *m_live on are bad rows.
 hipError_t launch_hash_prep(const Geom& g, const engram_hash_tables& t, int32_t* state,
                             const int32_t* ids, int B, int T, const uint8_t* scales,
                             const uint16_t* q, const uint16_t* k, void* scratch, uint32_t* err,
-                            hipStream_t s);
+                            hipStream_t s, const int32_t* live_idx = nullptr,
+                            const int* m_live = nullptr);
 
 // number of compute units of the current device (cached)
 int cu_count();
@@ -115,9 +131,12 @@ hipError_t launch_wkv_gate_partials(const Geom& g, const int32_t* hash_ids, cons
 // Stage 4 from the partial sums: per (token, stream) S_hh from x, S_kk and
 // S_hwk as the fixed-order sum of the dim/128 partials, then g and
 // out = bf16(h + g*v).
+// live_idx (with mask): v and part hold compacted rows, position m's at row
+// live_idx[m]
 hipError_t launch_gate_from_partials(const Geom& g, const uint16_t* x, const uint16_t* v,
                                      const float2* part, const uint8_t* mask, int64_t n_tok,
-                                     uint16_t* out, float* gate, hipStream_t s);
+                                     uint16_t* out, float* gate, hipStream_t s,
+                                     const int32_t* live_idx = nullptr);
 
 hipError_t launch_gate_add(const Geom& g, const uint16_t* x, const uint16_t* kv,
                            const uint16_t* q, const uint16_t* k, const uint8_t* mask,

@@ -163,6 +163,13 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
             tile_at<G_GROUP_M>(t, tiles_m, tiles_n, mt, nt);
         }
     };
+    // compacted rows: only the first *gp.m_live rows hold positions; the
+    // persistent order is laid over just the tiles that reach them, a single
+    // tile past them ends at once
+    const int m_live = gp.m_live ? *gp.m_live : 0;
+    if (P && gp.m_live) tiles_m = min(tiles_m, (m_live + BT - 1) / BT);
+    // every position live: the row map is the identity, skip its loads
+    const int32_t* rowmap = (gp.rowmap && m_live < M) ? gp.rowmap : nullptr;
     int m0c, n0c, m0n, n0n;
     {
         int mt, nt;
@@ -171,6 +178,7 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
             tile_coords(0, &mt, &nt);
         } else {
             if (!tile_of<G_GROUP_M>(blockIdx.x, per_xcd, tiles_m, tiles_n, &mt, &nt)) return;
+            if (gp.m_live && mt * BT >= m_live) return;
         }
         m0c = m0n = mt * BT;
         n0c = n0n = nt * BT;
@@ -445,7 +453,10 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
 #pragma unroll
             for (int i = 0; i < TI; ++i) {
                 const int64_t m = (int64_t)m0c + wm * WM + i * 32 + lrow;
-                const uint32_t xr = (uint32_t)(((m * gp.hc + s) * gp.dim + f0) * 2);
+                // the position of row m (compacted: from the row map, which
+                // points rows past the live count past x, where loads read 0)
+                const int64_t xm = rowmap ? (int64_t)rowmap[m] : m;
+                const uint32_t xr = (uint32_t)(((xm * gp.hc + s) * gp.dim + f0) * 2);
                 // all of the row's h values for this lane first (one round trip)
                 u32x2 hx[TJ * 4];
 #pragma unroll
@@ -618,11 +629,12 @@ __global__ void __launch_bounds__(256, 1)
 wkv_gathered_128(const uint32_t* __restrict__ aoff, const float2* __restrict__ scl, int n_cols,
                  int64_t m_pad, const uint8_t* __restrict__ table, int64_t num_rows,
                  const uint16_t* __restrict__ W, int64_t M, int N, uint16_t* __restrict__ C,
-                 int64_t ldc, int tiles_m, int tiles_n, int per_xcd) {
+                 int64_t ldc, int tiles_m, int tiles_n, int per_xcd, const int* m_live) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM128];
-    const GatePartials none{};
+    GatePartials lim{};
+    lim.m_live = m_live;
     gathered_tile<128, 2, 2, L, false>(aoff, scl, n_cols, m_pad, table, num_rows, W, M, N, C, ldc,
-                                       tiles_m, tiles_n, per_xcd, none, smem);
+                                       tiles_m, tiles_n, per_xcd, lim, smem);
 }
 
 // decode-sized batches: 64 x 64 tiles, two waves of 32 x 64, so that a
@@ -645,7 +657,7 @@ template <int L>
 hipError_t run_gathered_l(int bt, const uint32_t* aoff, const float2* scl, int n_cols,
                           int64_t m_pad, const uint8_t* table, int64_t num_rows,
                           const uint16_t* w, int64_t M, int N, uint16_t* c, int64_t ldc,
-                          hipStream_t s) {
+                          hipStream_t s, const int* m_live) {
     const int tiles_m = (int)((M + bt - 1) / bt);
     const int tiles_n = (N + bt - 1) / bt;
     const int total = tiles_m * tiles_n;
@@ -659,21 +671,28 @@ hipError_t run_gathered_l(int bt, const uint32_t* aoff, const float2* scl, int n
             aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, tiles_m, tiles_n, per_xcd);
     else
         wkv_gathered_128<L><<<dim3(per_xcd * N_XCD), dim3(256), 0, s>>>(
-            aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, tiles_m, tiles_n, per_xcd);
+            aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, tiles_m, tiles_n, per_xcd,
+            m_live);
     return hipGetLastError();
 }
 
 hipError_t run_gathered(int bt, const uint32_t* aoff, const float2* scl, int n_cols,
                         int64_t m_pad, const uint8_t* table, int64_t num_rows, const uint16_t* w,
-                        int64_t M, int N, uint16_t* c, int64_t ldc, hipStream_t s) {
+                        int64_t M, int N, uint16_t* c, int64_t ldc, hipStream_t s,
+                        const int* m_live = nullptr) {
+    // m_live (compacted rows) is honoured by the 128-wide tiles only
+    if (m_live && bt != 128) return hipErrorInvalidValue;
     const int L = n_cols <= 2 ? n_cols : 3 + n_cols % 3;
+#define ENGRAM_RUN_L(V) \
+    run_gathered_l<V>(bt, aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, s, m_live)
     switch (L) {
-        case 1: return run_gathered_l<1>(bt, aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, s);
-        case 2: return run_gathered_l<2>(bt, aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, s);
-        case 3: return run_gathered_l<3>(bt, aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, s);
-        case 4: return run_gathered_l<4>(bt, aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, s);
-        default: return run_gathered_l<5>(bt, aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, s);
+        case 1: return ENGRAM_RUN_L(1);
+        case 2: return ENGRAM_RUN_L(2);
+        case 3: return ENGRAM_RUN_L(3);
+        case 4: return ENGRAM_RUN_L(4);
+        default: return ENGRAM_RUN_L(5);
     }
+#undef ENGRAM_RUN_L
 }
 
 // Persistent 256x256 launch: one workgroup per compute unit (a multiple of 8,
@@ -810,6 +829,9 @@ hipError_t launch_wkv_gate_partials(const Geom& g, const int32_t* hash_ids, cons
                                     uint32_t* err, hipStream_t s, bool prepared) {
     if (M == 0) return hipSuccess;
     if (!gate_partials_supported(g, M) || gp.dim != g.dim || gp.hc != g.hc) return hipErrorInvalidValue;
+    // compacted rows come only from the hash's own placement
+    if ((gp.m_live == nullptr) != (gp.rowmap == nullptr) || (gp.m_live && !prepared))
+        return hipErrorInvalidValue;
     const GatheredScratch gs = gathered_scratch(g, M, scratch);
     const int64_t m_pad = gs.m_pad;
     uint32_t* aoff = gs.aoff;
@@ -828,7 +850,8 @@ hipError_t launch_wkv_gate_partials(const Geom& g, const int32_t* hash_ids, cons
                        cus, gpw, s);
     if (e != hipSuccess || nbig >= g.N) return e;
     return run_gathered(128, aoff, scl, g.n_cols, m_pad, table, g.num_embeddings,
-                        w + (int64_t)nbig * g.K, M, g.N - nbig, v + (nbig - kcols), g.dim, s);
+                        w + (int64_t)nbig * g.K, M, g.N - nbig, v + (nbig - kcols), g.dim, s,
+                        gp.m_live);
 }
 
 }  // namespace engram

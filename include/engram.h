@@ -190,7 +190,8 @@ engram_status engram_gate_from_partials(const engram_geometry* g, const uint16_t
                                         float* gate, void* stream);
 
 /* Bytes of workspace engram_forward needs for n_tok = B*T positions
- * (hash ids, gathered rows or the fused projection's scratch, and kv). */
+ * (hash ids, gathered rows or the fused projection's scratch, kv, and the
+ * live-position maps of a masked call). */
 size_t engram_forward_workspace_size(const engram_geometry* g, int64_t n_tok);
 
 /* The whole forward ([block] Engram.forward with the hash in front):
@@ -198,7 +199,14 @@ size_t engram_forward_workspace_size(const engram_geometry* g, int64_t n_tok);
  * engram_wkv_gathered where it applies.  Arguments as in the stage calls;
  * x, out: [B, T, hc_mult, dim]; ids, mask: [B, T]; gate: [B, T, hc_mult].
  * workspace: device memory of at least engram_forward_workspace_size bytes,
- * 256-byte aligned. */
+ * 256-byte aligned.
+ * With a mask, where the fully fused path applies (see
+ * engram_gate_partials_supported) only the live positions are hashed into
+ * the projection: they are packed in order, and the projection's tiles past
+ * the live count are skipped.  Masked positions still have their token ids
+ * and hashes checked (ENGRAM_ERRBIT_TOKEN, ENGRAM_ERRBIT_HASH); as their rows
+ * are never read they do not set ENGRAM_ERRBIT_ROW.  Every output is the same
+ * as without the packing. */
 engram_status engram_forward(const engram_geometry* g, const engram_hash_tables* t,
                              const uint8_t* table, const uint8_t* scales, const uint16_t* w,
                              const uint16_t* q, const uint16_t* k, int32_t* state,

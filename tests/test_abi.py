@@ -54,7 +54,8 @@ def test_derived_sizes():
     g = good()
     assert (g.n_hash_cols, g.K, g.N) == (24, 1536, 25600)
     ws = ge.engram_forward_workspace_size(g, 4096)
-    assert ws == 4096 * 24 * 4 + 4096 * 1536 * 2 + 4096 * 25600 * 2
+    # hash ids, rows (or the fused scratch), kv, and the live-row maps
+    assert ws == 4096 * 24 * 4 + 4096 * 1536 * 2 + 4096 * 25600 * 2 + 4096 * 4 + 4096 * 4 + 256
     assert ge.engram_forward_workspace_size(g, 0) == 0
 
 

@@ -299,3 +299,73 @@ def test_forward_equals_stage_calls(ge, dev, shape, B, T):
     assert torch.equal(state_a, state_b)
     assert torch.equal(out_a.view(torch.int16).reshape(-1), out_b.view(torch.int16).reshape(-1))
     assert torch.equal(gate_a.reshape(-1), gate_b.reshape(-1))
+
+
+# ------------------------------------------------------------------ masked prefill, compacted
+# Under a mask the fully fused forward projects only the live positions,
+# packed in order; the projection's tiles past the live count are skipped.
+# Its out, gate and state must equal, bit for bit, the dense stage calls
+# (every row projected) followed by the masked gate.  Mask patterns: spans
+# of 256..1024 positions (30% masked), everything masked, one live
+# position, every other position, a live count that leaves most
+# workgroups of the persistent kernel with no tile or one, and no position
+# masked.
+MASKS = ["spans", "none_live", "one_live", "alternate", "head300", "all_live"]
+
+
+def _mask(kind, cfg, T):
+    if kind == "spans":
+        return synth.token_mask(dataclasses.replace(cfg, mask_frac=0.3), 1, T)[0]
+    m = np.zeros(T, dtype=bool)
+    if kind == "one_live":
+        m[T // 3] = True
+    elif kind == "alternate":
+        m[::2] = True
+    elif kind == "head300":
+        m[:300] = True
+    elif kind == "all_live":
+        m[:] = True
+    return m
+
+
+@pytest.mark.parametrize("kind,T", [(k, 4096) for k in MASKS] + [("spans", 9000),
+                                                                 ("alternate", 9000)])
+def test_forward_masked_compaction(ge, dev, kind, T):
+    # T = 9000: the compaction's 4096-position blocks, with a ragged last one
+    cfg = dataclasses.replace(synth.config("tiny"), dim=2048, hc_mult=4, max_ngram_size=3,
+                              n_heads=3, head_dim=64, scale_codes=(120, 132), T=T)
+    wl = Workload(ge, cfg, dev)
+    g = wl.g
+    assert ge.engram_gate_partials_supported(g, T)
+    say("masked compaction", kind, T)
+    mask_np = _mask(kind, cfg, T)
+    ids_np = synth.token_ids(cfg, 1, T, name="mc")
+    masked = np.nonzero(~mask_np)[0]
+    if len(masked):
+        ids_np[0, masked[len(masked) // 2]] = cfg.vocab + 5   # a bad token at a masked position
+    ids = torch.from_numpy(ids_np).to(dev)
+    mask = torch.from_numpy(mask_np).to(dev)
+    x = synth.activations(cfg, T, dev, name="mcx").reshape(1, T, cfg.hc_mult, cfg.dim)
+    st0 = torch.from_numpy(synth.token_ids(cfg, 1, 2, name="mcs") % 500).to(dev)
+
+    state_a, err_a = st0.clone(), torch.zeros(1, dtype=torch.int32, device=dev)
+    gate_a = torch.full((1, T, cfg.hc_mult), -1.0, dtype=torch.float32, device=dev)
+    out_a = ge.engram_forward(g, wl.tables, wl.table, wl.scales, wl.w, wl.q, wl.k, x, ids,
+                              mask=mask, state=state_a, gate=gate_a, err=err_a)
+
+    state_b, err_b = st0.clone(), torch.zeros(1, dtype=torch.int32, device=dev)
+    gate_b = torch.full((T, cfg.hc_mult), -1.0, dtype=torch.float32, device=dev)
+    hid = ge.engram_hash(g, wl.tables, ids, state=state_b, err=err_b).reshape(T, -1)
+    xf = x.reshape(T, cfg.hc_mult, cfg.dim)
+    v, part = ge.engram_wkv_gate_partials(g, wl.table, wl.scales, hid, wl.w, xf, wl.q, wl.k,
+                                          err=err_b)
+    out_b = ge.engram_gate_from_partials(g, xf, v, part, mask=mask, gate=gate_b)
+    torch.cuda.synchronize()
+    assert int(err_a.item()) == int(err_b.item()) == (ge.ERRBIT_TOKEN if len(masked) else 0)
+    assert torch.equal(state_a, state_b)
+    assert torch.equal(out_a.view(torch.int16).reshape(-1), out_b.view(torch.int16).reshape(-1))
+    assert torch.equal(gate_a.reshape(-1), gate_b.reshape(-1))
+    # masked positions: x itself and gate 0
+    mk = torch.from_numpy(~mask_np).to(dev)
+    assert torch.equal(out_a[0][mk].view(torch.int16), x[0][mk].view(torch.int16))
+    assert torch.all(gate_a[0][mk] == 0).item()
