@@ -43,11 +43,13 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run 3 plain device copies of exactly 1 GiB (a known-size kernel "
                         "against which HBM byte counters are scaled)")
-    p.add_argument("--workload", choices=("prefill", "decode", "long_mixed"), default="prefill",
+    p.add_argument("--workload", choices=("prefill", "decode", "long_mixed", "hash_layers"),
+                   default="prefill",
                    help="prefill (the default and the headline line); decode: 128 steps "
                         "of 64 sequences after a 512-token prefill, replayed as one graph; "
                         "long_mixed: T=32768 with Zipf(1.1) ids and 30%% of positions masked "
-                        "in spans")
+                        "in spans; hash_layers: 8 Engram layers' hashes of the T=4096 prefill "
+                        "in one launch")
     p.add_argument("--summarize", nargs=3, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR"),
                    help="no GPU work: turn the CSV output of three rocprofv3 runs of this "
                         "script (--kernel-trace --stats; --pmc FETCH_SIZE; --pmc WRITE_SIZE, "
@@ -224,6 +226,9 @@ def main():
         return
     if args.workload == "long_mixed":
         long_mixed(args)
+        return
+    if args.workload == "hash_layers":
+        hash_layers(args)
         return
     import numpy as np
     import torch
@@ -533,6 +538,63 @@ def long_mixed(args):
         "dense_stage_calls_ms": round(sec_dense * 1e3, 4),
         "live_projection_ms": round(sec_proj * 1e3, 4),
         "wall_s": round(wall, 3),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def hash_layers(args):
+    """Eight Engram layers' hashes of the T=4096 prefill: one engram_hash_layers
+    launch against eight engram_hash calls (each layer with its own tables and
+    table size, drawn like the prefill's with a seed of its own).  Bytes per
+    call: ids once, token ids and table reads from L2, 96 B of hash ids per
+    position and layer written."""
+    import dataclasses
+
+    import torch
+
+    import gram_memory_layer_amd as ge
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    base = synth.config("prefill")
+    n_layers = 8
+    geoms, tabs = [], []
+    for l in range(n_layers):
+        cfg = dataclasses.replace(base, index=200 + l)
+        t = synth.hash_tables(cfg)
+        geoms.append(ge.Geometry.make(cfg.dim, cfg.hc_mult, cfg.max_ngram_size, cfg.n_heads,
+                                      cfg.head_dim, t["num_embeddings"], cfg.vocab, cfg.pad_id,
+                                      cfg.norm_eps))
+        tabs.append({k: torch.from_numpy(t[k]).to(dev)
+                     for k in ("token_map", "mult", "prime", "offset")})
+    B, T = base.B, base.T
+    ids = torch.from_numpy(synth.token_ids(base, B, T)).to(dev)
+    out = torch.empty((n_layers, B, T, geoms[0].n_hash_cols), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def one():
+        ge.engram_hash_layers(geoms, tabs, ids, hash_ids=out)
+
+    def separate():
+        for l in range(n_layers):
+            ge.engram_hash(geoms[l], tabs[l], ids, hash_ids=out[l])
+
+    one()
+    separate()
+    torch.cuda.synchronize()
+    steps = max(args.steps, 20)
+    sec = time_launches(one, steps, stream)
+    sec_sep = time_launches(separate, steps, stream)
+    rec = {
+        "metric": "Engram hash of 8 layers, positions/s (1 GPU), T=4096",
+        "value": round(B * T / sec, 1), "unit": "positions/s", "n_gpus": 1, "steps": steps,
+        "warmup": 1, "ms_per_step": round(sec * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int64", "data": "synthetic",
+        "config": {"workload": "hash ids of 8 Engram layers (own tables each), B=1 T=4096, "
+                               "24 hash columns", "global_batch": B, "seq_len": T,
+                   "parallelism": "single GPU"},
+        "separate_calls_ms": round(sec_sep * 1e3, 4),
     }
     print(json.dumps(rec), flush=True)
 

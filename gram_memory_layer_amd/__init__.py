@@ -24,7 +24,7 @@ import torch
 
 __all__ = [
     "Geometry", "HashTables", "EngramError", "EngramLayer", "load", "library_path",
-    "engram_check_geometry", "engram_hash", "engram_gather", "engram_wkv",
+    "engram_check_geometry", "engram_hash", "engram_hash_layers", "engram_gather", "engram_wkv",
     "engram_wkv_gathered", "engram_wkv_gathered_scratch_size",
     "engram_gate_partials_supported", "engram_wkv_gate_partials", "engram_gate_from_partials",
     "engram_gate_add", "engram_forward", "engram_forward_workspace_size",
@@ -98,6 +98,8 @@ def load():
     L.engram_check_geometry.argtypes = [G]
     L.engram_hash.restype = C.c_int
     L.engram_hash.argtypes = [G, HT, P, P, i32, i32, P, P, P]
+    L.engram_hash_layers.restype = C.c_int
+    L.engram_hash_layers.argtypes = [G, HT, i32, P, P, i32, i32, P, P, P]
     L.engram_gather.restype = C.c_int
     L.engram_gather.argtypes = [G, P, P, P, i64, P, P, P]
     L.engram_wkv.restype = C.c_int
@@ -190,6 +192,38 @@ def engram_hash(g: Geometry, tables: dict, ids: torch.Tensor, state=None, hash_i
         _dev(err, "err", torch.int32, (1,), dev)
     _check("engram_hash", L.engram_hash(C.byref(g), C.byref(ht), _ptr(state), ids.data_ptr(), B, T,
                                         hash_ids.data_ptr(), _ptr(err), _stream(dev)))
+    return hash_ids
+
+
+def engram_hash_layers(geoms, tables, ids: torch.Tensor, states=None, hash_ids=None, err=None):
+    """Several layers' hashes in one launch: geoms / tables are lists (one
+    per layer; only num_embeddings and the tables may differ), ids int32
+    [B, T] -> hash_ids int32 [n_layers, B, T, n_hash_cols]; `states` None or a
+    list of per-layer int32 [B, max_ngram_size-1] states, updated in place."""
+    L = load()
+    dev = ids.device
+    _dev(ids, "ids", torch.int32, None, dev)
+    if ids.dim() != 2:
+        raise ValueError("ids must be [B, T]")
+    n = len(geoms)
+    if len(tables) != n or (states is not None and len(states) != n):
+        raise ValueError("one geometry, table set and state per layer")
+    B, T = ids.shape
+    g0 = geoms[0]
+    garr = (Geometry * n)(*geoms)
+    tarr = (HashTables * n)(*[_tables(tables[l], geoms[l], dev) for l in range(n)])
+    sarr = None
+    if states is not None:
+        for st in states:
+            _dev(st, "state", torch.int32, (B, g0.max_ngram_size - 1), dev)
+        sarr = (C.c_void_p * n)(*[st.data_ptr() for st in states])
+    if hash_ids is None:
+        hash_ids = torch.empty((n, B, T, g0.n_hash_cols), dtype=torch.int32, device=dev)
+    _dev(hash_ids, "hash_ids", torch.int32, (n, B, T, g0.n_hash_cols), dev)
+    if err is not None:
+        _dev(err, "err", torch.int32, (1,), dev)
+    _check("engram_hash_layers", L.engram_hash_layers(
+        garr, tarr, n, sarr, ids.data_ptr(), B, T, hash_ids.data_ptr(), _ptr(err), _stream(dev)))
     return hash_ids
 
 

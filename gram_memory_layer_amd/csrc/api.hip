@@ -84,6 +84,42 @@ engram_status engram_hash(const engram_geometry* g, const engram_hash_tables* t,
                                         (hipStream_t)stream));
 }
 
+engram_status engram_hash_layers(const engram_geometry* geoms, const engram_hash_tables* tables,
+                                 int32_t n_layers, int32_t* const* states, const int32_t* ids,
+                                 int32_t B, int32_t T, int32_t* hash_ids, uint32_t* err,
+                                 void* stream) {
+    if (geoms == nullptr || tables == nullptr) return ENGRAM_ERR_INVALID_ARG;
+    if (n_layers < 1 || n_layers > engram::kMaxHashLayers) return ENGRAM_ERR_INVALID_ARG;
+    int64_t num_emb[engram::kMaxHashLayers];
+    for (int l = 0; l < n_layers; ++l) {
+        const engram_status st = engram_check_geometry(&geoms[l]);
+        if (st != ENGRAM_OK) return st;
+        // every field the hash reads, except the table size, is shared
+        const engram_geometry& a = geoms[0];
+        const engram_geometry& b = geoms[l];
+        if (b.max_ngram_size != a.max_ngram_size || b.n_heads != a.n_heads ||
+            b.vocab != a.vocab || b.pad_id != a.pad_id)
+            return ENGRAM_ERR_INVALID_ARG;
+        const engram_hash_tables& t = tables[l];
+        if (!t.token_map || !t.mult || !t.prime || !t.offset) return ENGRAM_ERR_INVALID_ARG;
+        num_emb[l] = b.num_embeddings;
+        if (states) {
+            if (states[l] == nullptr) return ENGRAM_ERR_INVALID_ARG;
+            for (int j = 0; j < l; ++j)
+                if (states[j] == states[l]) return ENGRAM_ERR_INVALID_ARG;  // updated in place
+        }
+    }
+    if (B < 0 || T < 0) return ENGRAM_ERR_INVALID_ARG;
+    const Geom gg = engram::make_geom(geoms[0]);
+    const int64_t per_layer = (int64_t)B * T * gg.n_cols;
+    if ((int64_t)B * T >= kMaxTokens || per_layer * n_layers >= ((int64_t)1 << 40))
+        return ENGRAM_ERR_INVALID_ARG;
+    if (per_layer == 0) return ENGRAM_OK;
+    if (!ids || !hash_ids) return ENGRAM_ERR_INVALID_ARG;
+    return from_hip(engram::launch_hash_layers(gg, tables, num_emb, n_layers, states, ids, B, T,
+                                               hash_ids, err, (hipStream_t)stream));
+}
+
 engram_status engram_gather(const engram_geometry* g, const uint8_t* table, const uint8_t* scales,
                             const int32_t* hash_ids, int64_t n_tok, uint16_t* rows,
                             uint32_t* err, void* stream) {

@@ -125,7 +125,7 @@ __device__ __forceinline__ void emit(const HashArgs& a, int64_t m, int col, int3
 }
 
 template <bool PREP>
-__global__ void __launch_bounds__(kThreads) hash_kernel(HashArgs a) {
+__device__ __forceinline__ void hash_work(const HashArgs& a) {
     const int n_state = a.max_ngram - 1;
     const int64_t M = (int64_t)a.B * a.T;
     // with a state, positions t < n_state belong to the head workgroups
@@ -198,6 +198,41 @@ __global__ void __launch_bounds__(kThreads) hash_kernel(HashArgs a) {
     if (bad && a.err) atomicOr(a.err, bad);
 }
 
+template <bool PREP>
+__global__ void __launch_bounds__(kThreads) hash_kernel(HashArgs a) {
+    hash_work<PREP>(a);
+}
+
+// Several layers' hashes in one launch: blockIdx.y picks the layer, whose
+// tables, state, table size and output replace the shared arguments'.
+struct LayerTables {
+    const int32_t* token_map;
+    const uint64_t* mult;
+    const uint64_t* prime;
+    const uint64_t* offset;
+    int32_t* state;
+    int32_t* hash_ids;
+    int64_t num_embeddings;
+};
+struct LayersArgs {
+    HashArgs shared;
+    LayerTables layer[kMaxHashLayers];
+};
+static_assert(sizeof(LayersArgs) <= 4096, "kernel argument budget");
+
+__global__ void __launch_bounds__(kThreads) hash_layers_kernel(LayersArgs la) {
+    HashArgs a = la.shared;
+    const LayerTables& l = la.layer[blockIdx.y];
+    a.token_map = l.token_map;
+    a.mult = l.mult;
+    a.prime = l.prime;
+    a.offset = l.offset;
+    a.state = l.state;
+    a.hash_ids = l.hash_ids;
+    a.num_embeddings = l.num_embeddings;
+    hash_work<false>(a);
+}
+
 HashArgs base_args(const Geom& g, const engram_hash_tables& t, int32_t* state, const int32_t* ids,
                    int B, int T, uint32_t* err) {
     HashArgs a{};
@@ -253,6 +288,27 @@ hipError_t launch_hash_prep(const Geom& g, const engram_hash_tables& t, int32_t*
     a.n_body = (int)((total + kThreads - 1) / kThreads);
     const int heads = state ? head_blocks(g, B, T, &a.seq_per_head) : 0;
     hash_kernel<true><<<dim3((unsigned)(a.n_body + heads)), dim3(kThreads), 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_hash_layers(const Geom& g, const engram_hash_tables* tables,
+                              const int64_t* num_embeddings, int n_layers, int32_t* const* states,
+                              const int32_t* ids, int B, int T, int32_t* hash_ids, uint32_t* err,
+                              hipStream_t s) {
+    const int64_t total = (int64_t)B * T * g.n_cols;
+    if (total == 0) return hipSuccess;
+    if (n_layers < 1 || n_layers > kMaxHashLayers) return hipErrorInvalidValue;
+    LayersArgs la{};
+    la.shared = base_args(g, tables[0], nullptr, ids, B, T, err);
+    la.shared.n_body = (int)((total + kThreads - 1) / kThreads);
+    const int heads = states ? head_blocks(g, B, T, &la.shared.seq_per_head) : 0;
+    for (int l = 0; l < n_layers; ++l) {
+        la.layer[l] = LayerTables{tables[l].token_map, tables[l].mult,    tables[l].prime,
+                                  tables[l].offset,    states ? states[l] : nullptr,
+                                  hash_ids + (int64_t)l * total, num_embeddings[l]};
+    }
+    hash_layers_kernel<<<dim3((unsigned)(la.shared.n_body + heads), (unsigned)n_layers),
+                         dim3(kThreads), 0, s>>>(la);
     return hipGetLastError();
 }
 

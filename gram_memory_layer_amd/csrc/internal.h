@@ -37,6 +37,16 @@ hipError_t launch_hash(const Geom& g, const engram_hash_tables& t, int32_t* stat
                        const int32_t* ids, int B, int T, int32_t* hash_ids, uint32_t* err,
                        hipStream_t s);
 
+// Several layers' stage 1 in one launch: layer l uses tables[l],
+// num_embeddings[l] and states[l] (states NULL, or every entry set and
+// distinct) and writes hash_ids + l * B*T*n_cols; the other geometry
+// fields are shared.
+constexpr int kMaxHashLayers = 32;
+hipError_t launch_hash_layers(const Geom& g, const engram_hash_tables* tables,
+                              const int64_t* num_embeddings, int n_layers, int32_t* const* states,
+                              const int32_t* ids, int B, int T, int32_t* hash_ids, uint32_t* err,
+                              hipStream_t s);
+
 hipError_t launch_gather(const Geom& g, const uint8_t* table, const uint8_t* scales,
                          const int32_t* hash_ids, int64_t n_tok, uint16_t* rows, uint32_t* err,
                          hipStream_t s);

@@ -101,6 +101,24 @@ engram_status engram_hash(const engram_geometry* g, const engram_hash_tables* t,
                           int32_t* state, const int32_t* ids, int32_t B, int32_t T,
                           int32_t* hash_ids, uint32_t* err, void* stream);
 
+/* Stage 1 for several Engram layers in one launch.  Each layer hashes with
+ * its own tables and table size ([block] constructor: the layer's
+ * layer_hash_index selects its num_embeddings; [docs] stage 1), while the
+ * token ids, and so all the index arithmetic, are shared.
+ *   geoms    n_layers geometries, equal in max_ngram_size, n_heads, vocab and
+ *            pad_id (num_embeddings may differ; the other fields are unused).
+ *   tables   n_layers table sets.
+ *   states   NULL, or a host array of n_layers distinct device pointers, each
+ *            as engram_hash's state for that layer.
+ *   hash_ids int32 [n_layers, B, T, n_hash_cols] out; layer l's block is what
+ *            engram_hash(geoms[l], tables[l], states[l], ...) writes.
+ * 1 <= n_layers <= 32.  Bit-exact (integer); the error word collects every
+ * layer's flags. */
+engram_status engram_hash_layers(const engram_geometry* geoms,
+                                 const engram_hash_tables* tables, int32_t n_layers,
+                                 int32_t* const* states, const int32_t* ids, int32_t B,
+                                 int32_t T, int32_t* hash_ids, uint32_t* err, void* stream);
+
 /* Stage 2: gather and dequantise table rows ([docs] stage 2, embed_rows,
  * regen_table; [block] self.embed).
  *   table    uint8 [num_embeddings, head_dim]      fp8 e4m3fn codes.

@@ -86,6 +86,35 @@ def test_host_side_rejections_launch_nothing():
     assert lib.engram_status_string(2) == b"unsupported geometry"
 
 
+def test_hash_layers_host_checks():
+    lib = ge.load()
+    fake = C.c_void_p(1 << 20)
+    n = 3
+    geoms = (ge.Geometry * n)(*[good() for _ in range(n)])
+    tabs = (ge.HashTables * n)(*[ge.HashTables(fake, fake, fake, fake) for _ in range(n)])
+
+    def call(n=n, geoms=geoms, tabs=tabs, states=None, B=1, T=8):
+        return lib.engram_hash_layers(geoms, tabs, n, states, fake, B, T, fake, None, None)
+    assert call(n=0) == 1
+    assert call(n=33) == 1
+    assert call(B=-1) == 1
+    assert call(tabs=None) == 1
+    g2 = (ge.Geometry * n)(*[good() for _ in range(n)])
+    g2[1].n_heads = 6                                     # shared index arithmetic differs
+    assert call(geoms=g2) == 1
+    g3 = (ge.Geometry * n)(*[good() for _ in range(n)])
+    g3[2].num_embeddings = 1000                           # table sizes may differ
+    assert call(geoms=g3, B=0) == 0
+    dup = (C.c_void_p * n)(fake, C.c_void_p((1 << 20) + 64), fake)
+    assert call(states=dup) == 1                          # states are updated in place
+    part = (C.c_void_p * n)(fake, None, C.c_void_p((1 << 20) + 64))
+    assert call(states=part) == 1
+    b = (ge.HashTables * n)(*[ge.HashTables(fake, fake, fake, fake) for _ in range(n)])
+    b[1].prime = None
+    assert call(tabs=b) == 1
+    assert call(B=0) == 0                                 # empty work: a no-op success
+
+
 def test_fused_projection_host_checks():
     lib = ge.load()
     g = good()

@@ -99,6 +99,46 @@ def test_hash_state_split_geometries(ge, dev, mx, nh, B, chunks):
     assert np.array_equal(state.cpu().numpy(), wl.t["token_map"][ids[:, T - (mx - 1):]])
 
 
+# Several layers in one launch: each layer's block of the output equals the
+# single-layer call with that layer's tables, table size and state (the
+# single-layer call is pinned to the oracle above).
+@pytest.mark.parametrize("n_layers,B,chunks,with_state", [(3, 5, (7, 1, 2), True),
+                                                          (4, 2, (300,), False),
+                                                          (32, 3, (5, 1), True)])
+def test_hash_layers_equal_single_calls(ge, dev, n_layers, B, chunks, with_state):
+    import dataclasses
+    base = dataclasses.replace(synth.config("tiny"), max_ngram_size=4, n_heads=3)
+    say("hash layers", n_layers, B, chunks, with_state)
+    cfgs = [dataclasses.replace(base, index=100 + l, prime_limit=1009 + 500 * l)
+            for l in range(n_layers)]
+    wls = [Workload(ge, c, dev, with_table=False, with_weights=False) for c in cfgs]
+    assert len({w.num_emb for w in wls}) > 1
+    T = sum(chunks)
+    ids = synth.token_ids(base, B, T, name="layers")
+    ids[0, 0] = base.vocab + 9                                # a bad token: flagged once
+    st_multi = [torch.full((B, 3), base.pad_id, dtype=torch.int32, device=dev) + l
+                for l in range(n_layers)] if with_state else None
+    st_single = [s.clone() for s in st_multi] if with_state else None
+    err_m = torch.zeros(1, dtype=torch.int32, device=dev)
+    err_s = torch.zeros(1, dtype=torch.int32, device=dev)
+    got, want, s0 = [], [], 0
+    for c in chunks:
+        part = torch.from_numpy(ids[:, s0:s0 + c].copy()).to(dev)
+        got.append(ge.engram_hash_layers([w.g for w in wls], [w.tables for w in wls], part,
+                                         states=st_multi, err=err_m))
+        want.append(torch.stack([ge.engram_hash(w.g, w.tables, part,
+                                                state=st_single[l] if with_state else None,
+                                                err=err_s)
+                                 for l, w in enumerate(wls)]))
+        s0 += c
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(got, dim=2), torch.cat(want, dim=2))
+    assert int(err_m.item()) == int(err_s.item()) == ge.ERRBIT_TOKEN
+    if with_state:
+        for a, b in zip(st_multi, st_single):
+            assert torch.equal(a, b)
+
+
 def test_hash_bad_token_flags_and_stays_in_range(ge, dev, tiny):
     say("hash bad token")
     ids = synth.token_ids(tiny.cfg, 1, 16, name="bad")
