@@ -55,7 +55,39 @@ def parse():
                         "script (--kernel-trace --stats; --pmc FETCH_SIZE; --pmc WRITE_SIZE, "
                         "the last two with --copy-calibration) into the summaries under "
                         "profiles/")
+    p.add_argument("--summarize-stats", nargs=3, metavar=("STATS_DIR", "NAME", "BENCH_ARGS"),
+                   help="no GPU work: turn one rocprofv3 --kernel-trace --stats run of "
+                        "`bench.py BENCH_ARGS` into profiles/NAME.txt")
     return p.parse_args()
+
+
+def summarize_stats(stats_dir, name, bench_args):
+    """Kernel table (calls, average, min, max, share) plus median durations
+    of the library's kernels, for any bench workload."""
+    rows = _csv(stats_dir, "kernel_stats.csv")
+    lines = ["# rocprofv3 kernel-trace statistics: python3 bench.py %s" % bench_args,
+             "# command (repository root = <repo>):",
+             "#   cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format "
+             "csv -d <out> -o <name> -- python3 <repo>/bench.py %s" % bench_args,
+             "# averages include every call (set-up and warm-up calls too).",
+             "",
+             "%-40s %7s %12s %12s %12s %7s" % ("kernel", "calls", "avg_ns", "min_ns", "max_ns", "pct")]
+    for r in rows:
+        lines.append("%-40s %7s %12.0f %12s %12s %7s" % (
+            short_name(r["Name"]), r["Calls"], float(r["AverageNs"]), r["MinNs"], r["MaxNs"],
+            r["Percentage"]))
+    durs = {}
+    for r in _csv(stats_dir, "kernel_trace.csv"):
+        if "engram::" in r["Kernel_Name"]:
+            durs.setdefault(short_name(r["Kernel_Name"]), []).append(
+                int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    lines.append("")
+    lines.append("# median ns per library kernel (kernel trace):")
+    for k, v in sorted(durs.items()):
+        lines.append("#   %-40s %10d  (%d calls)" % (k, sorted(v)[len(v) // 2], len(v)))
+    out = os.path.join(ROOT, "profiles", name + ".txt")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("wrote", os.path.relpath(out, ROOT))
 
 
 def kernel_source_digest() -> str:
@@ -215,6 +247,9 @@ def main():
     args = parse()
     if args.summarize:
         summarize(*args.summarize)
+        return
+    if args.summarize_stats:
+        summarize_stats(*args.summarize_stats)
         return
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: every box in this setup has one, and the "
