@@ -58,12 +58,13 @@ def _check_against_oracle_and_two_stage(ge, g, cfg, table, scales, hid, w, sampl
     return tolerances.check_kv(got, ref, absdot, g.K)
 
 
-# (dim, hc, max_ngram, n_heads): K = 64 * (max_ngram-1) * n_heads covers 1..8
-# k-tiles (every prologue and drain sequence of the 3-stage ring, with and
-# without a pass of the steady loop); N = dim*(hc+1) covers whole and ragged
-# 256- and 128-wide tiles.
+# (dim, hc, max_ngram, n_heads): K = 64 * (max_ngram-1) * n_heads covers 1..12
+# and 17 k-tiles: every prologue and drain sequence of the 3-stage ring, with
+# and without passes of the steady loop; N = dim*(hc+1) covers whole and
+# ragged 256-, 128- and 64-wide tiles.
 GEOMS = [(256, 3, 2, 1), (200, 4, 3, 1), (256, 1, 2, 3), (512, 2, 3, 2), (96, 4, 5, 1),
-         (128, 2, 6, 1), (320, 4, 4, 2), (64, 1, 8, 1), (256, 3, 5, 2)]
+         (128, 2, 6, 1), (320, 4, 4, 2), (64, 1, 8, 1), (256, 3, 5, 2), (64, 2, 4, 3),
+         (128, 1, 6, 2), (64, 1, 12, 1), (96, 2, 5, 3), (64, 1, 2, 17)]
 
 
 @pytest.mark.parametrize("shape", GEOMS)
