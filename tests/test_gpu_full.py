@@ -273,6 +273,56 @@ def test_decode_graph_replay(ge, dev):
         _ = (xs[0].float() * 2).sum().item()  # eager work between replays
 
 
+def test_masked_prefill_graph_replay(ge, dev):
+    # the fully fused prefill under a mask (live-row compaction, hash into
+    # compact rows, persistent projection over the live tiles, gate from the
+    # partial sums) captured once and replayed three times, with the mask
+    # changed between replays through its own buffer: every replay must match
+    # an eager forward with that mask bit for bit
+    import dataclasses
+    T = 4096
+    cfg = dataclasses.replace(synth.config("prefill"), dim=2048, n_heads=3, T=T, mask_frac=0.3)
+    wl = Workload(ge, cfg, dev)
+    assert ge.engram_gate_partials_supported(wl.g, T)
+    ids = torch.from_numpy(synth.token_ids(cfg, 1, T)).to(dev)
+    x = synth.activations(cfg, T, dev).reshape(1, T, cfg.hc_mult, cfg.dim)
+    masks = [torch.from_numpy(synth.token_mask(cfg, 1, T, name="gm%d" % r)).to(dev)
+             for r in range(3)]
+    layer = ge.EngramLayer(wl.g, wl.tables, wl.table, wl.scales, wl.w, wl.q, wl.k)
+    ws = layer.workspace(T)
+    mask = masks[0].clone()
+    out_g = torch.empty_like(x)
+    gate_g = torch.empty((1, T, cfg.hc_mult), dtype=torch.float32, device=dev)
+
+    def run(m, out, gate):
+        ge.engram_forward(wl.g, wl.tables, wl.table, wl.scales, wl.w, wl.q, wl.k, x, ids, mask=m,
+                          out=out, gate=gate, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(mask, out_g, gate_g)  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(mask, out_g, gate_g)
+    for rep in range(3):
+        say("masked prefill graph: replay", rep)
+        out_e = torch.empty_like(x)
+        gate_e = torch.empty_like(gate_g)
+        run(masks[rep], out_e, gate_e)
+        torch.cuda.synchronize()
+        mask.copy_(masks[rep])
+        out_g.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g.view(torch.int16), out_e.view(torch.int16)), rep
+        assert torch.equal(gate_g, gate_e), rep
+        _ = (x.float() * 2).sum().item()  # eager work between replays
+
+
 # ------------------------------------------------------------------ gate stress
 def test_gate_stress_full(ge, dev):
     cfg = synth.config("gate_stress")
