@@ -14,7 +14,7 @@ import torch
 import oracle
 import synth
 from tests import tolerances
-from tests.gpu_util import Workload, bits, say
+from tests.gpu_util import Workload, bits, geometry, say
 
 pytestmark = pytest.mark.gpu
 
@@ -321,6 +321,80 @@ def test_masked_prefill_graph_replay(ge, dev):
         assert torch.equal(out_g.view(torch.int16), out_e.view(torch.int16)), rep
         assert torch.equal(gate_g, gate_e), rep
         _ = (x.float() * 2).sum().item()  # eager work between replays
+
+
+# ------------------------------------------------------------------ maximum sizes
+def test_forward_largest_fused_prefill(ge, dev):
+    # the longest sequence the fully fused path takes at dim 5120, hc 4 (x
+    # must fit one 32-bit buffer descriptor: T * 4 * 5120 * 2 < 2^32), with
+    # 30% of positions masked in spans; sampled positions against the oracle
+    # (the last ones included), masked positions pass x through
+    import dataclasses
+    T = ((1 << 32) - 1) // (4 * 5120 * 2)
+    cfg = dataclasses.replace(synth.config("prefill"), T=T, mask_frac=0.3)
+    wl = Workload(ge, cfg, dev)
+    assert ge.engram_gate_partials_supported(wl.g, T)
+    assert not ge.engram_gate_partials_supported(wl.g, T + 1)
+    say("largest fused prefill, T =", T)
+    ids_np = synth.token_ids(cfg, 1, T)
+    ids = torch.from_numpy(ids_np).to(dev)
+    x = synth.activations(cfg, T, dev).reshape(1, T, cfg.hc_mult, cfg.dim)
+    mask_np = synth.token_mask(cfg, 1, T)
+    mask = torch.from_numpy(mask_np).to(dev)
+    gate = torch.empty((1, T, cfg.hc_mult), dtype=torch.float32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    layer = ge.EngramLayer(wl.g, wl.tables, wl.table, wl.scales, wl.w, wl.q, wl.k)
+    out = layer.forward(x, ids, mask=mask, gate=gate, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    mk = mask_np.reshape(-1)
+    live = np.nonzero(mk)[0]
+    pos = np.unique(np.concatenate([live[:3], live[-3:], _sample_positions(T, n=10, seed=11)]))
+    pos = pos[mk[pos]]
+    xb = bits(x.reshape(T, cfg.hc_mult, cfg.dim)[torch.from_numpy(pos).to(dev)])
+    ref = _oracle_tokens(wl, ids_np[0], pos, xb, mk[pos])
+    ref["_q"], ref["_k"] = bits(wl.q), bits(wl.k)
+    ob = bits(out.reshape(T, cfg.hc_mult, cfg.dim)[torch.from_numpy(pos).to(dev)])
+    gs, os_ = _check_tokens(ref, ob, gate.reshape(T, -1)[torch.from_numpy(pos).to(dev)].cpu().numpy(),
+                            xb, cfg)
+    say("   gate", gs, "out", os_)
+    m = torch.from_numpy(~mk).to(dev)
+    assert torch.equal(out.reshape(T, -1)[m].view(torch.int16), x.reshape(T, -1)[m].view(torch.int16))
+
+
+def test_fused_table_offsets_past_2gib(ge, dev):
+    # a 60M-row table (3.84 GB): row byte offsets beyond 2^31 go through the
+    # unsigned 32-bit buffer offsets of the fused loader and the gather
+    import dataclasses
+    rows = 60_000_000
+    cfg = dataclasses.replace(synth.config("tiny"), dim=256, hc_mult=1, max_ngram_size=2,
+                              n_heads=3, head_dim=64, scale_codes=(120, 132))
+    g = geometry(ge, cfg, rows)
+    say("table past 2 GiB:", rows, "rows")
+    table, scales = synth.embedding_table(cfg, rows, dev, chunk_rows=1 << 22)
+    w = synth.wkv_weight(cfg, dev)
+    rng = np.random.default_rng(5)
+    for M in (100, 2048):
+        hid_np = rng.integers(rows - 200_000, rows, (M, g.n_hash_cols)).astype(np.int32)
+        hid_np[0, 0] = rows - 1
+        hid_np[1, 0] = 0
+        hid = torch.from_numpy(hid_np).to(dev)
+        err = torch.zeros(1, dtype=torch.int32, device=dev)
+        kv = ge.engram_wkv_gathered(g, table, scales, hid, w, err=err)
+        two = ge.engram_wkv(g, ge.engram_gather(g, table, scales, hid), w)
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
+        assert torch.equal(kv.view(torch.int16), two.view(torch.int16)), M
+        pos = np.array([0, 1, M // 2, M - 1])
+        uniq, inv = np.unique(hid_np[pos].reshape(-1), return_inverse=True)
+        idx = torch.from_numpy(uniq.astype(np.int64)).to(dev)
+        r = oracle.embed_rows(table.index_select(0, idx).cpu().numpy(),
+                              scales.index_select(0, idx).cpu().numpy(),
+                              inv.reshape(len(pos), -1).astype(np.int32)).reshape(len(pos), -1)
+        ref = oracle.linear(r, bits(w))
+        absdot = np.abs(tolerances.bf16_value(r)) @ np.abs(tolerances.bf16_value(bits(w))).T
+        tolerances.check_kv(bits(kv[torch.from_numpy(pos).to(dev)]), ref, absdot, g.K)
+    del table, scales
 
 
 # ------------------------------------------------------------------ gate stress
