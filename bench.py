@@ -55,6 +55,9 @@ def parse():
                         "script (--kernel-trace --stats; --pmc FETCH_SIZE; --pmc WRITE_SIZE, "
                         "the last two with --copy-calibration) into the summaries under "
                         "profiles/")
+    p.add_argument("--summarize-counters", nargs=3, metavar=("PMC_DIR", "NAME", "ROCPROF_ARGS"),
+                   help="no GPU work: turn one rocprofv3 --pmc run of the prefill bench into "
+                        "profiles/NAME.txt")
     p.add_argument("--summarize-stats", nargs=3, metavar=("STATS_DIR", "NAME", "BENCH_ARGS"),
                    help="no GPU work: turn one rocprofv3 --kernel-trace --stats run of "
                         "`bench.py BENCH_ARGS` into profiles/NAME.txt")
@@ -88,6 +91,48 @@ def summarize_stats(stats_dir, name, bench_args):
     out = os.path.join(ROOT, "profiles", name + ".txt")
     open(out, "w").write("\n".join(lines) + "\n")
     print("wrote", os.path.relpath(out, ROOT))
+
+
+def summarize_counters(pmc_dir, name, rocprof_args):
+    """Mean of each collected counter per library kernel, from one rocprofv3
+    --pmc run of the prefill bench, with the derived clock and matrix-core
+    busy share where GRBM_GUI_ACTIVE and SQ_VALU_MFMA_BUSY_CYCLES are present
+    (GUI_ACTIVE is summed over the 8 XCDs; the busy cycles over the 1024
+    SIMDs)."""
+    per = {}
+    for r in _csv(pmc_dir, "counter_collection.csv"):
+        if "engram::" not in r["Kernel_Name"]:
+            continue
+        k = short_name(r["Kernel_Name"])
+        d = per.setdefault(k, {"_dur": {}})
+        d.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        d["_dur"][r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    lines = ["# rocprofv3 counters per dispatch (mean over dispatches): Engram prefill bench",
+             "# command (repository root = <repo>):",
+             "#   cd /tmp && export TMPDIR=/tmp && rocprofv3 %s --output-format csv -d <out> "
+             "-o <name> -- python3 <repo>/bench.py --no-cpu-baseline --steps 5 --warmup 3"
+             % rocprof_args, ""]
+    for k in sorted(per):
+        d = per[k]
+        durs = sorted(d.pop("_dur").values())
+        med = durs[len(durs) // 2]
+        lines.append("%s  (%d dispatches, median %.1f us)" % (k, len(durs), med / 1e3))
+        for c in sorted(d):
+            lines.append("    %-28s %14.4g" % (c, sum(d[c]) / len(d[c])))
+        if "GRBM_GUI_ACTIVE" in d:
+            gui = sum(d["GRBM_GUI_ACTIVE"]) / len(d["GRBM_GUI_ACTIVE"]) / N_XCD_COUNT
+            lines.append("    clock (GUI_ACTIVE per XCD / median time)   %.2f GHz" % (gui / med))
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in d:
+                busy = sum(d["SQ_VALU_MFMA_BUSY_CYCLES"]) / len(d["SQ_VALU_MFMA_BUSY_CYCLES"])
+                lines.append("    matrix cores busy (busy / SIMDs / cycles)  %.1f %%"
+                             % (100.0 * busy / SIMD_COUNT / gui))
+    out = os.path.join(ROOT, "profiles", name + ".txt")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("wrote", os.path.relpath(out, ROOT))
+
+
+N_XCD_COUNT = 8       # MI355X XCDs
+SIMD_COUNT = 1024     # 256 CUs x 4 SIMDs
 
 
 def kernel_source_digest() -> str:
@@ -250,6 +295,9 @@ def main():
         return
     if args.summarize_stats:
         summarize_stats(*args.summarize_stats)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
         return
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: every box in this setup has one, and the "
