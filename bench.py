@@ -389,6 +389,22 @@ def main():
     st_gate = time_launches(lambda: ge.engram_gate_add(g, x, kv, q, k, mask=mask, out=out), reps,
                             stream)
 
+    # the same forward with the caches cold: a 512 MiB write (past the 256 MB
+    # MALL and the 8 x 4 MB L2) between forwards, each forward timed alone
+    flush = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
+    cold = []
+    for _ in range(10):
+        flush.fill_(1)
+        s0 = torch.cuda.Event(enable_timing=True)
+        s1 = torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        step()
+        s1.record(stream)
+        s1.synchronize()
+        cold.append(s0.elapsed_time(s1))
+    del flush
+    cold_ms = sorted(cold)[len(cold) // 2]
+
     flops_per_token = 2 * g.K * g.N
     wkv_flops = flops_per_token * n_tok
     achieved = wkv_flops / st_proj / 1e12
@@ -426,6 +442,7 @@ def main():
         "gate_hbm": {"kernel": "engram_gate_from_partials",
                      "achieved": round(gate_bytes / st_pgate / 1e9, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(gate_bytes / st_pgate / 1e9 / PEAK_HBM_GBS, 4)},
+        "ms_per_step_cold_caches": round(cold_ms, 4),
         "wall_s": round(wall, 3),
     }
 
