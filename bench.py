@@ -300,8 +300,9 @@ def main():
         summarize_counters(*args.summarize_counters)
         return
     if args.gpus != 1:
-        print("bench.py runs on exactly one GPU: every box in this setup has one, and the "
-              "Engram path is measured per GPU (see DESIGN.md for how it would shard).",
+        print("bench.py measures one GPU only: the Engram path is built and timed per GPU "
+              "(split across GPUs it would take whole sequences, or token ranges plus a "
+              "look-back halo of raw ids, per GPU, with no activation exchange).",
               file=sys.stderr)
         sys.exit(2)
     if args.workload == "decode":
