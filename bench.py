@@ -40,6 +40,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=2048, help="tokens the oracle runs")
+    p.add_argument("--cpu-threads", type=int, default=0,
+                   help="threads for the oracle timing (default: all the host offers)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run 3 plain device copies of exactly 1 GiB (a known-size kernel "
                         "against which HBM byte counters are scaled)")
@@ -458,6 +460,9 @@ def main():
         del src, dst
 
     if not args.no_cpu_baseline:
+        if args.cpu_threads > 0:
+            import oracle
+            oracle.set_num_threads(args.cpu_threads)
         rec["cpu_baseline"] = cpu_baseline(cfg, t, table, scales, w, q, k, x, ids_np, mask,
                                            args.cpu_sample)
     print(json.dumps(rec), flush=True)

@@ -49,6 +49,8 @@ def lib():
         P = C.c_void_p
         i64, i32 = C.c_int64, C.c_int32
         L.eo_num_threads.restype = C.c_int
+        L.eo_set_num_threads.restype = None
+        L.eo_set_num_threads.argtypes = [C.c_int]
         L.eo_bf16_value.restype = C.c_double
         L.eo_bf16_value.argtypes = [C.c_uint16]
         L.eo_bf16_round.restype = C.c_uint16
@@ -87,6 +89,11 @@ def _c(a, dtype):
 
 def num_threads() -> int:
     return lib().eo_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops (timing only)."""
+    lib().eo_set_num_threads(int(n))
 
 
 # ------------------------------------------------------------------ codecs

@@ -51,6 +51,16 @@ int eo_num_threads(void) {
 #endif
 }
 
+/* Threads for the parallel loops that follow (timing only; results do not
+ * depend on it: every output element is computed by one thread). */
+void eo_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------ bf16 */
 
 /* Value of a bf16 bit pattern: the top half of an IEEE binary32. */
