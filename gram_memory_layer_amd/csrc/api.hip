@@ -300,16 +300,12 @@ engram_status engram_forward(const engram_geometry* g, const engram_hash_tables*
         float2* part = reinterpret_cast<float2*>(
             reinterpret_cast<char*>(kv) + align256((size_t)n_tok * gg.dim * sizeof(uint16_t)));
         engram::GatePartials gp{x, q, k, part, gg.dim, gg.hc};
-        hipError_t e = hipSuccess;
         if (mask) {
-            e = engram::launch_live_rows(mask, n_tok, engram::padded_rows(n_tok), live_idx, rowmap,
-                                         m_live, s);
             gp.m_live = m_live;
             gp.rowmap = rowmap;
         }
-        if (e == hipSuccess)
-            e = engram::launch_hash_prep(gg, *t, state, ids, B, T, scales, q, k, rows, err, s,
-                                         mask ? live_idx : nullptr, mask ? m_live : nullptr);
+        hipError_t e = engram::launch_hash_prep(gg, *t, state, ids, B, T, scales, q, k, rows, err,
+                                                s, mask, live_idx, rowmap, m_live);
         if (e == hipSuccess)
             e = engram::launch_wkv_gate_partials(gg, nullptr, table, scales, w, n_tok, gp, v, rows,
                                                  err, s, /*prepared=*/true);

@@ -73,6 +73,14 @@ struct HashArgs {
     // compacted rows (masked prefill): live positions go to row live_idx[m]
     const int32_t* live_idx;
     const int* m_live;
+    // or the compaction done here (fuse_mask): each workgroup counts the live
+    // positions before its rows itself; the maps are written as by
+    // launch_live_rows
+    const uint8_t* mask;
+    int32_t* live_out;
+    int32_t* rowmap_out;
+    int* m_live_out;
+    int fuse_mask, mask16;
 };
 
 // Hash id of column col at position t of sequence b (the unsigned 64-bit
@@ -98,18 +106,9 @@ __device__ __forceinline__ int32_t hash_at(const HashArgs& a, int b, int t, int 
 // the offsets-and-scales form a hash outside the table is also a bad row, as
 // it is when the ids pass through memory to the projection; with compacted
 // rows a masked position is not placed (and its row never read).
-template <bool PREP>
-__device__ __forceinline__ void emit(const HashArgs& a, int64_t m, int col, int32_t id,
-                                     uint32_t* bad) {
-    if (!PREP) {
-        a.hash_ids[m * a.n_cols + col] = id;
-        return;
-    }
-    int64_t r = m;
-    if (a.live_idx && *a.m_live < a.B * (int64_t)a.T) {  // (all live: the identity)
-        r = a.live_idx[m];
-        if (r < 0) return;
-    }
+// The row offset and scales of hash id `id` at projection row r.
+__device__ __forceinline__ void place(const HashArgs& a, int64_t r, int col, int32_t id,
+                                      uint32_t* bad) {
     uint32_t off = kBadRowOffset;
     float2 sc = make_float2(0.0f, 0.0f);
     if (id >= 0) {
@@ -125,6 +124,92 @@ __device__ __forceinline__ void emit(const HashArgs& a, int64_t m, int col, int3
 }
 
 template <bool PREP>
+__device__ __forceinline__ void emit(const HashArgs& a, int64_t m, int col, int32_t id,
+                                     uint32_t* bad) {
+    if (!PREP) {
+        a.hash_ids[m * a.n_cols + col] = id;
+        return;
+    }
+    int64_t r = m;
+    if (a.live_idx && *a.m_live < a.B * (int64_t)a.T) {  // (all live: the identity)
+        r = a.live_idx[m];
+        if (r < 0) return;
+    }
+    place(a, r, col, id, bad);
+}
+
+// Nonzero bytes in a word.
+__device__ __forceinline__ int live_bytes(uint32_t w) {
+    const uint32_t z = ~(((w & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | w | 0x7F7F7F7Fu);  // 0x80 per zero byte
+    return 4 - __popc(z);
+}
+
+// Body workgroup of the fused compaction: rows m0 .. m0+255 of one column.
+// Every thread takes part (two workgroup barriers), so nothing returns early.
+__device__ __forceinline__ void body_fused(const HashArgs& a, int body_from, uint32_t* bad) {
+    __shared__ int red[kThreads / 64], wl[kThreads / 64];
+    const int64_t M = (int64_t)a.B * a.T;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int64_t g0 = (int64_t)blockIdx.x * kThreads;
+    const int col = (int)(g0 / a.m_pad);
+    const int64_t m0 = g0 - (int64_t)col * a.m_pad;  // a multiple of 256, below M
+    const int64_t m = m0 + tid;
+    // live positions before this block (m0 is a multiple of 16)
+    int cnt = 0;
+    if (a.mask16) {
+        for (int64_t j = 16 * (int64_t)tid; j < m0; j += 16 * kThreads) {
+            const uint4 v = *reinterpret_cast<const uint4*>(a.mask + j);
+            cnt += live_bytes(v.x) + live_bytes(v.y) + live_bytes(v.z) + live_bytes(v.w);
+        }
+    } else {
+        for (int64_t j = 4 * (int64_t)tid; j < m0; j += 4 * kThreads)
+            cnt += live_bytes(*reinterpret_cast<const uint32_t*>(a.mask + j));
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
+    const bool live = m < M && a.mask[m] != 0;
+    const uint64_t bal = __ballot(live);
+    if (lane == 0) {
+        red[wv] = cnt;
+        wl[wv] = __popcll(bal);
+    }
+    __syncthreads();
+    int64_t pre = 0, blk = 0, before = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) {
+        pre += red[w];
+        blk += wl[w];
+        before += w < wv ? wl[w] : 0;
+    }
+    const int64_t slot = pre + before + __popcll(bal & ((1ull << lane) - 1ull));
+    if (col == 0) {
+        if (m < M) a.live_out[m] = live ? (int32_t)slot : -1;
+        if (live) a.rowmap_out[slot] = (int32_t)m;
+    }
+    if (m0 + kThreads >= M) {
+        // the block holding the last position: the live count is known here;
+        // rows tot .. ceil256(tot)-1 are the only rows past it the projection
+        // reads, so they are the ones marked bad
+        const int64_t tot = pre + blk;
+        const int64_t r = tot + tid;
+        if (r < (tot + 255) / 256 * 256) {
+            a.aoff[(int64_t)col * a.m_pad + r] = kBadRowOffset;
+            a.scl[(int64_t)col * a.m_pad + r] = make_float2(0.0f, 0.0f);
+            if (col == 0) a.rowmap_out[r] = (int32_t)M;
+        }
+        if (col == 0 && tid == 0) *a.m_live_out = (int)tot;
+    }
+    if (m < M) {
+        const int b = (int)(m / a.T);
+        const int t = (int)(m - (int64_t)b * a.T);
+        if (t >= body_from) {
+            const int32_t id = hash_at(a, b, t, col, bad);
+            if (live) place(a, slot, col, id, bad);
+        }
+    }
+}
+
+template <bool PREP>
 __device__ __forceinline__ void hash_work(const HashArgs& a) {
     const int n_state = a.max_ngram - 1;
     const int64_t M = (int64_t)a.B * a.T;
@@ -137,6 +222,13 @@ __device__ __forceinline__ void hash_work(const HashArgs& a) {
             for (int64_t j = i; j < a.nqk; j += (int64_t)a.n_body * kThreads)
                 a.wqk[j] = __uint_as_float((uint32_t)a.q[j] << 16) *
                            __uint_as_float((uint32_t)a.k[j] << 16);
+        if constexpr (PREP) {
+            if (a.fuse_mask) {
+                body_fused(a, body_from, &bad);
+                if (bad && a.err) atomicOr(a.err, bad);
+                return;
+            }
+        }
         int64_t m;
         int col;
         if (PREP) {  // rows fastest, padded rows included
@@ -184,7 +276,17 @@ __device__ __forceinline__ void hash_work(const HashArgs& a) {
             const int b = b0 + r / hh;
             const int t = r % hh;
             const int32_t id = hash_at(a, b, t, col, &bad);
-            emit<PREP>(a, (int64_t)b * a.T + t, col, id, &bad);
+            if (PREP && a.fuse_mask) {
+                // one sequence (B = 1): the compact row of position t counts
+                // the live positions before it
+                if (a.mask[t] != 0) {
+                    int slot = 0;
+                    for (int u = 0; u < t; ++u) slot += a.mask[u] != 0;
+                    place(a, slot, col, id, &bad);
+                }
+            } else {
+                emit<PREP>(a, (int64_t)b * a.T + t, col, id, &bad);
+            }
         }
         // every state read of these sequences is above this barrier
         __syncthreads();
@@ -268,14 +370,34 @@ int head_blocks(const Geom& g, int B, int T, int* seq_per_head) {
 hipError_t launch_hash_prep(const Geom& g, const engram_hash_tables& t, int32_t* state,
                             const int32_t* ids, int B, int T, const uint8_t* scales,
                             const uint16_t* q, const uint16_t* k, void* scratch, uint32_t* err,
-                            hipStream_t s, const int32_t* live_idx, const int* m_live) {
+                            hipStream_t s, const uint8_t* mask, int32_t* live_idx,
+                            int32_t* rowmap, int* m_live) {
     const int64_t M = (int64_t)B * T;
     if (M == 0) return hipSuccess;
-    if ((live_idx == nullptr) != (m_live == nullptr)) return hipErrorInvalidValue;
+    if (mask && (!live_idx || !rowmap || !m_live)) return hipErrorInvalidValue;
     const GatheredScratch gs = gathered_scratch(g, M, scratch);
     HashArgs a = base_args(g, t, state, ids, B, T, err);
-    a.live_idx = live_idx;
-    a.m_live = m_live;
+    if (mask) {
+        // Short sequences count the live positions in every workgroup (each
+        // reads the mask up to its own rows); longer ones, several sequences
+        // with a state, or a mask not 4-byte aligned take the one-workgroup
+        // scan first.
+        const bool fuse = M <= kFusedCompactionMax && (state == nullptr || B == 1) &&
+                          ((uintptr_t)mask & 3u) == 0;
+        if (fuse) {
+            a.fuse_mask = 1;
+            a.mask16 = ((uintptr_t)mask & 15u) == 0;
+            a.mask = mask;
+            a.live_out = live_idx;
+            a.rowmap_out = rowmap;
+            a.m_live_out = m_live;
+        } else {
+            const hipError_t e = launch_live_rows(mask, M, gs.m_pad, live_idx, rowmap, m_live, s);
+            if (e != hipSuccess) return e;
+            a.live_idx = live_idx;
+            a.m_live = m_live;
+        }
+    }
     a.scales = scales;
     a.m_pad = gs.m_pad;
     a.aoff = gs.aoff;

@@ -108,14 +108,19 @@ __device__ __forceinline__ float e8m0_scale(uint32_t c) {
 // themselves are not written): for every position and hash column, the row
 // offset and scales; q*k as well when q is given; the state updated as in
 // launch_hash.
-// With live_idx (from launch_live_rows), live positions go to their compact
-// rows and masked ones are hashed (their token and hash checks still flag)
-// but not placed; compact rows from *m_live on are bad rows.
+// With a mask, the live positions are packed in order: live_idx, rowmap and
+// *m_live are written as by launch_live_rows (by that kernel first, or, for
+// short single sequences, by the hash kernel itself), live positions go to
+// their compact rows, masked ones are hashed (their token and hash checks
+// still flag) but not placed, and the compact rows past the live count that
+// the projection reads are bad rows.
+constexpr int64_t kFusedCompactionMax = 32768;
 hipError_t launch_hash_prep(const Geom& g, const engram_hash_tables& t, int32_t* state,
                             const int32_t* ids, int B, int T, const uint8_t* scales,
                             const uint16_t* q, const uint16_t* k, void* scratch, uint32_t* err,
-                            hipStream_t s, const int32_t* live_idx = nullptr,
-                            const int* m_live = nullptr);
+                            hipStream_t s, const uint8_t* mask = nullptr,
+                            int32_t* live_idx = nullptr, int32_t* rowmap = nullptr,
+                            int* m_live = nullptr);
 
 // number of compute units of the current device (cached)
 int cu_count();

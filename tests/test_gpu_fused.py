@@ -329,28 +329,40 @@ def _mask(kind, cfg, T):
     return m
 
 
-@pytest.mark.parametrize("kind,T", [(k, 4096) for k in MASKS] + [("spans", 9000),
-                                                                 ("alternate", 9000)])
-def test_forward_masked_compaction(ge, dev, kind, T):
-    # T = 9000: the compaction's 4096-position blocks, with a ragged last one
+# Layouts: one sequence with the mask 16-byte aligned (the hash kernel counts
+# the live positions itself, 16 bytes a load), 4-byte aligned (4 bytes a
+# load), or at an odd address, and two sequences with a state (those two take
+# the one-workgroup scan before the hash).
+@pytest.mark.parametrize("kind,T,layout", [(k, 4096, "b1") for k in MASKS] +
+                         [("spans", 9000, "b1"), ("alternate", 9000, "b1"),
+                          ("spans", 4096, "b2"), ("alternate", 4096, "off1"),
+                          ("spans", 9000, "off4"), ("spans", 40000, "b1")])
+def test_forward_masked_compaction(ge, dev, kind, T, layout):
+    # T = 9000: a ragged last 256-row block; T = 40000: past the positions
+    # the hash kernel counts itself
+    B = 2 if layout == "b2" else 1
+    Tb = T // B
     cfg = dataclasses.replace(synth.config("tiny"), dim=2048, hc_mult=4, max_ngram_size=3,
                               n_heads=3, head_dim=64, scale_codes=(120, 132), T=T)
     wl = Workload(ge, cfg, dev)
     g = wl.g
     assert ge.engram_gate_partials_supported(g, T)
-    say("masked compaction", kind, T)
+    say("masked compaction", kind, T, layout)
     mask_np = _mask(kind, cfg, T)
-    ids_np = synth.token_ids(cfg, 1, T, name="mc")
+    ids_np = synth.token_ids(cfg, 1, T, name="mc").reshape(B, Tb)
     masked = np.nonzero(~mask_np)[0]
     if len(masked):
-        ids_np[0, masked[len(masked) // 2]] = cfg.vocab + 5   # a bad token at a masked position
+        ids_np.reshape(-1)[masked[len(masked) // 2]] = cfg.vocab + 5   # bad token, masked position
     ids = torch.from_numpy(ids_np).to(dev)
-    mask = torch.from_numpy(mask_np).to(dev)
-    x = synth.activations(cfg, T, dev, name="mcx").reshape(1, T, cfg.hc_mult, cfg.dim)
-    st0 = torch.from_numpy(synth.token_ids(cfg, 1, 2, name="mcs") % 500).to(dev)
+    off = {"off1": 1, "off4": 4}.get(layout, 0)
+    mbuf = torch.zeros(T + 16, dtype=torch.uint8, device=dev)
+    mbuf[off:off + T] = torch.from_numpy(mask_np.astype(np.uint8)).to(dev)
+    mask = mbuf[off:off + T].view(B, Tb)
+    x = synth.activations(cfg, T, dev, name="mcx").reshape(B, Tb, cfg.hc_mult, cfg.dim)
+    st0 = torch.from_numpy(synth.token_ids(cfg, B, 2, name="mcs") % 500).to(dev)
 
     state_a, err_a = st0.clone(), torch.zeros(1, dtype=torch.int32, device=dev)
-    gate_a = torch.full((1, T, cfg.hc_mult), -1.0, dtype=torch.float32, device=dev)
+    gate_a = torch.full((B, Tb, cfg.hc_mult), -1.0, dtype=torch.float32, device=dev)
     out_a = ge.engram_forward(g, wl.tables, wl.table, wl.scales, wl.w, wl.q, wl.k, x, ids,
                               mask=mask, state=state_a, gate=gate_a, err=err_a)
 
@@ -360,7 +372,8 @@ def test_forward_masked_compaction(ge, dev, kind, T):
     xf = x.reshape(T, cfg.hc_mult, cfg.dim)
     v, part = ge.engram_wkv_gate_partials(g, wl.table, wl.scales, hid, wl.w, xf, wl.q, wl.k,
                                           err=err_b)
-    out_b = ge.engram_gate_from_partials(g, xf, v, part, mask=mask, gate=gate_b)
+    out_b = ge.engram_gate_from_partials(g, xf, v, part, mask=mask.reshape(-1).contiguous(),
+                                         gate=gate_b)
     torch.cuda.synchronize()
     assert int(err_a.item()) == int(err_b.item()) == (ge.ERRBIT_TOKEN if len(masked) else 0)
     assert torch.equal(state_a, state_b)
@@ -368,5 +381,6 @@ def test_forward_masked_compaction(ge, dev, kind, T):
     assert torch.equal(gate_a.reshape(-1), gate_b.reshape(-1))
     # masked positions: x itself and gate 0
     mk = torch.from_numpy(~mask_np).to(dev)
-    assert torch.equal(out_a[0][mk].view(torch.int16), x[0][mk].view(torch.int16))
-    assert torch.all(gate_a[0][mk] == 0).item()
+    assert torch.equal(out_a.reshape(T, -1)[mk].view(torch.int16),
+                       x.reshape(T, -1)[mk].view(torch.int16))
+    assert torch.all(gate_a.reshape(T, -1)[mk] == 0).item()
