@@ -16,7 +16,8 @@
 //               past the table for a bad id or a padding row: reads as 0),
 //   scl[c][m]   the row's two 32-block scales 2^(s-127) as fp32,
 // so that the projection's per-k-tile fetches are contiguous and it does no
-// id checks or scale decoding in its inner loop.
+// id checks or scale decoding in its inner loop.  (The forward skips it: its
+// hash kernel writes these arrays directly.)
 //
 // LDS: each of the three ring stages is made of 1 KiB blocks (one buffer DMA
 // instruction each: 16 fp8 A rows, or 8 W rows of 128 bytes) plus 256 bytes
