@@ -138,10 +138,17 @@ SIMD_COUNT = 1024     # 256 CUs x 4 SIMDs
 
 
 def kernel_source_digest() -> str:
+    """Digest of the fused projection's sources with comments and blank
+    lines dropped: the counted traffic stays valid across comment edits."""
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gram_memory_layer_amd", "csrc")
     for f in ("wkv_gathered.hip", "tiles.h", "internal.h"):
-        h.update(open(os.path.join(csrc, f), "rb").read())
+        src = open(os.path.join(csrc, f)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", "", src)
+        src = "\n".join(l.rstrip() for l in src.splitlines() if l.strip())
+        h.update(src.encode())
     return h.hexdigest()[:16]
 
 
