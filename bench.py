@@ -45,13 +45,15 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run 3 plain device copies of exactly 1 GiB (a known-size kernel "
                         "against which HBM byte counters are scaled)")
-    p.add_argument("--workload", choices=("prefill", "decode", "long_mixed", "hash_layers"),
+    p.add_argument("--workload", choices=("prefill", "decode", "long_mixed", "hash_layers",
+                                          "gate_stress"),
                    default="prefill",
                    help="prefill (the default and the headline line); decode: 128 steps "
                         "of 64 sequences after a 512-token prefill, replayed as one graph; "
                         "long_mixed: T=32768 with Zipf(1.1) ids and 30%% of positions masked "
                         "in spans; hash_layers: 8 Engram layers' hashes of the T=4096 prefill "
-                        "in one launch")
+                        "in one launch; gate_stress: the gate and add alone over 65,536 tokens "
+                        "of given kv")
     p.add_argument("--summarize", nargs=3, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR"),
                    help="no GPU work: turn the CSV output of three rocprofv3 runs of this "
                         "script (--kernel-trace --stats; --pmc FETCH_SIZE; --pmc WRITE_SIZE, "
@@ -322,6 +324,9 @@ def main():
         return
     if args.workload == "hash_layers":
         hash_layers(args)
+        return
+    if args.workload == "gate_stress":
+        gate_stress(args)
         return
     import numpy as np
     import torch
@@ -708,6 +713,55 @@ def hash_layers(args):
                                "24 hash columns", "global_batch": B, "seq_len": T,
                    "parallelism": "single GPU"},
         "separate_calls_ms": round(sec_sep * 1e3, 4),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def gate_stress(args):
+    """The gate and add alone (engram_gate_add) over B=8 x T=8192 tokens whose
+    kv is given: keys built from the stream (25% exactly orthogonal under the
+    weights, 15% near-zero dot products, the rest c*x + noise), value N(0,1).
+    Algorithmic bytes: x and kv read, out written = 133,120 B per token
+    (8.72 GB)."""
+    import torch
+
+    import gram_memory_layer_amd as ge
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = synth.config("gate_stress")
+    t = synth.hash_tables(cfg)
+    g = ge.Geometry.make(cfg.dim, cfg.hc_mult, cfg.max_ngram_size, cfg.n_heads, cfg.head_dim,
+                         t["num_embeddings"], cfg.vocab, cfg.pad_id, cfg.norm_eps)
+    n = cfg.n_tokens
+    x = synth.activations(cfg, n, dev)
+    q, k = synth.qk_weights(cfg, dev)
+    kv, _ = synth.gate_stress_kv(cfg, x, q, k)
+    out = torch.empty_like(x)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        ge.engram_gate_add(g, x, kv, q, k, out=out)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    steps = max(args.steps // 5, 10)
+    sec = time_launches(step, steps, stream)
+    nbytes = n * (2 * cfg.hc_mult * cfg.dim * 2 + g.N * 2)
+    gbs = nbytes / sec / 1e9
+    rec = {
+        "metric": "Engram gate and add GB/s @dim5120 hc4 (1 GPU), 65,536 tokens",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": 3,
+        "ms_per_step": round(sec * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "Engram gate and add alone, B=8 T=8192, dim=5120 hc=4, given kv "
+                               "(orthogonal, near-zero and scaled keys)",
+                   "global_batch": cfg.B, "seq_len": cfg.T, "parallelism": "single GPU"},
+        "roofline": {"kernel": "engram_gate_add", "bound": "hbm", "achieved": round(gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": None},
     }
     print(json.dumps(rec), flush=True)
 
