@@ -27,7 +27,7 @@ __all__ = [
     "engram_check_geometry", "engram_hash", "engram_hash_layers", "engram_gather", "engram_wkv",
     "engram_wkv_gathered", "engram_wkv_gathered_scratch_size",
     "engram_gate_partials_supported", "engram_wkv_gate_partials", "engram_gate_from_partials",
-    "engram_gate_add", "engram_forward", "engram_forward_workspace_size",
+    "engram_gate_add", "engram_forward", "engram_forward_hashed", "engram_forward_workspace_size",
     "ERRBIT_TOKEN", "ERRBIT_HASH", "ERRBIT_ROW",
 ]
 
@@ -116,6 +116,8 @@ def load():
     L.engram_gate_from_partials.argtypes = [G, P, P, P, P, i64, P, P, P]
     L.engram_gate_add.restype = C.c_int
     L.engram_gate_add.argtypes = [G, P, P, P, P, P, i64, P, P, P]
+    L.engram_forward_hashed.restype = C.c_int
+    L.engram_forward_hashed.argtypes = [G, P, P, P, P, P, P, P, P, i64, P, P, P, C.c_size_t, P, P]
     L.engram_forward_workspace_size.restype = C.c_size_t
     L.engram_forward_workspace_size.argtypes = [G, i64]
     L.engram_forward.restype = C.c_int
@@ -434,6 +436,46 @@ def engram_forward(g: Geometry, tables: dict, table, scales, w, q, k, x, ids, ma
         C.byref(g), C.byref(ht), table.data_ptr(), scales.data_ptr(), w.data_ptr(), q.data_ptr(),
         k.data_ptr(), _ptr(state), x.data_ptr(), ids.data_ptr(), _ptr(m), B, T, out.data_ptr(),
         _ptr(gate), workspace.data_ptr(), workspace.numel(), _ptr(err), _stream(dev)))
+    return out
+
+
+def engram_forward_hashed(g: Geometry, table, scales, w, q, k, x, hash_ids, mask=None, out=None,
+                          gate=None, workspace=None, err=None):
+    """The forward from given hash ids (the block's forward signature): x bf16
+    [..., hc, dim], hash_ids int32 [..., n_hash_cols] (same leading shape),
+    mask bool/uint8 over the positions or None -> out (like x)."""
+    L = load()
+    dev = x.device
+    _dev(hash_ids, "hash_ids", torch.int32, None, dev)
+    n_tok = hash_ids.numel() // g.n_hash_cols
+    if hash_ids.numel() != n_tok * g.n_hash_cols or hash_ids.shape[-1] != g.n_hash_cols:
+        raise ValueError("hash_ids must be [..., n_hash_cols]")
+    _dev(x, "x", torch.bfloat16, None, dev)
+    if x.numel() != n_tok * g.hc_mult * g.dim or x.shape[-1] != g.dim:
+        raise ValueError("x must be [..., hc_mult, dim] with one position per hash-id row")
+    _dev(table, "table", torch.uint8, (g.num_embeddings, g.head_dim), dev)
+    _dev(scales, "scales", torch.uint8, (g.num_embeddings, g.head_dim // 32), dev)
+    _dev(w, "w", torch.bfloat16, (g.N, g.K), dev)
+    _dev(q, "q", torch.bfloat16, (g.hc_mult, g.dim), dev)
+    _dev(k, "k", torch.bfloat16, (g.hc_mult, g.dim), dev)
+    m = _mask(mask, n_tok, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _dev(out, "out", torch.bfloat16, tuple(x.shape), dev)
+    if gate is not None:
+        _dev(gate, "gate", torch.float32, None, dev)
+        if gate.numel() != n_tok * g.hc_mult:
+            raise ValueError("gate must hold n_tok*hc_mult values")
+    need = engram_forward_workspace_size(g, n_tok)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev(workspace, "workspace", torch.uint8, None, dev)
+    if err is not None:
+        _dev(err, "err", torch.int32, (1,), dev)
+    _check("engram_forward_hashed", L.engram_forward_hashed(
+        C.byref(g), table.data_ptr(), scales.data_ptr(), w.data_ptr(), q.data_ptr(), k.data_ptr(),
+        x.data_ptr(), hash_ids.data_ptr(), _ptr(m), n_tok, out.data_ptr(), _ptr(gate),
+        workspace.data_ptr(), workspace.numel(), _ptr(err), _stream(dev)))
     return out
 
 

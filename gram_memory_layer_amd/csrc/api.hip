@@ -331,4 +331,75 @@ engram_status engram_forward(const engram_geometry* g, const engram_hash_tables*
     return from_hip(e);
 }
 
+engram_status engram_forward_hashed(const engram_geometry* g, const uint8_t* table,
+                                    const uint8_t* scales, const uint16_t* w, const uint16_t* q,
+                                    const uint16_t* k, const uint16_t* x, const int32_t* hash_ids,
+                                    const uint8_t* mask, int64_t n_tok, uint16_t* out, float* gate,
+                                    void* workspace, size_t workspace_bytes, uint32_t* err,
+                                    void* stream) {
+    engram_status st = engram_check_geometry(g);
+    if (st != ENGRAM_OK) return st;
+    if (n_tok < 0 || n_tok >= kMaxTokens) return ENGRAM_ERR_INVALID_ARG;
+    if (n_tok == 0) return ENGRAM_OK;
+    if (!hash_ids || !table || !scales || !w || !q || !k || !x || !out)
+        return ENGRAM_ERR_INVALID_ARG;
+    if (((uintptr_t)table & 7u) != 0 || !aligned16(w) || !aligned16(q) || !aligned16(k) ||
+        !aligned16(x) || !aligned16(out))
+        return ENGRAM_ERR_INVALID_ARG;
+    const size_t need = engram_forward_workspace_size(g, n_tok);
+    if (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
+        return ENGRAM_ERR_WORKSPACE;
+    const Geom gg = engram::make_geom(*g);
+    // the same workspace layout as engram_forward (its hash-id region unused)
+    char* ws = (char*)workspace;
+    ws += align256((size_t)n_tok * gg.n_cols * sizeof(int32_t));
+    uint16_t* rows = (uint16_t*)ws;
+    {
+        const size_t rb = (size_t)n_tok * gg.K * sizeof(uint16_t);
+        const size_t sb = engram::gathered_scratch_bytes(gg, n_tok);
+        ws += align256(rb > sb ? rb : sb);
+    }
+    uint16_t* kv = (uint16_t*)ws;
+    ws += align256((size_t)n_tok * gg.N * sizeof(uint16_t));
+    int32_t* live_idx = (int32_t*)ws;
+    ws += align256((size_t)n_tok * sizeof(int32_t));
+    int32_t* rowmap = (int32_t*)ws;
+    ws += align256((size_t)engram::padded_rows(n_tok) * sizeof(int32_t));
+    int* m_live = (int*)ws;
+    hipStream_t s = (hipStream_t)stream;
+    const bool fused = (n_tok >= 1024 || n_tok <= 256) && aligned16(table) &&
+                       engram::gathered_supported(gg, n_tok);
+    hipError_t e = hipSuccess;
+    if (fused && engram::gate_partials_supported(gg, n_tok)) {
+        uint16_t* v = kv;
+        float2* part = reinterpret_cast<float2*>(
+            reinterpret_cast<char*>(kv) + align256((size_t)n_tok * gg.dim * sizeof(uint16_t)));
+        engram::GatePartials gp{x, q, k, part, gg.dim, gg.hc};
+        if (mask) {
+            e = engram::launch_live_rows(mask, n_tok, engram::padded_rows(n_tok), live_idx,
+                                         rowmap, m_live, s);
+            gp.m_live = m_live;
+            gp.rowmap = rowmap;
+        }
+        if (e == hipSuccess)
+            e = engram::launch_prep_scratch(gg, hash_ids, scales, n_tok, rows, err, s, q, k,
+                                            mask ? live_idx : nullptr, mask ? m_live : nullptr);
+        if (e == hipSuccess)
+            e = engram::launch_wkv_gate_partials(gg, nullptr, table, scales, w, n_tok, gp, v, rows,
+                                                 err, s, /*prepared=*/true);
+        if (e == hipSuccess)
+            e = engram::launch_gate_from_partials(gg, x, v, part, mask, n_tok, out, gate, s,
+                                                  mask ? live_idx : nullptr);
+        return from_hip(e);
+    }
+    if (fused) {
+        e = engram::launch_wkv_gathered(gg, hash_ids, table, scales, w, n_tok, kv, rows, err, s);
+    } else {
+        e = engram::launch_gather(gg, table, scales, hash_ids, n_tok, rows, err, s);
+        if (e == hipSuccess) e = engram::launch_wkv(rows, w, n_tok, gg.N, gg.K, kv, s);
+    }
+    if (e == hipSuccess) e = engram::launch_gate_add(gg, x, kv, q, k, mask, n_tok, out, gate, s);
+    return from_hip(e);
+}
+
 }  // extern "C"

@@ -122,6 +122,15 @@ hipError_t launch_hash_prep(const Geom& g, const engram_hash_tables& t, int32_t*
                             int32_t* live_idx = nullptr, int32_t* rowmap = nullptr,
                             int* m_live = nullptr);
 
+// The fused projections' scratch from given hash ids [M][n_cols] (what the
+// stage calls' own prep does); with q, also q*k; with live_idx and m_live
+// (from launch_live_rows), live positions at their compact rows as in
+// launch_hash_prep.
+hipError_t launch_prep_scratch(const Geom& g, const int32_t* hash_ids, const uint8_t* scales,
+                               int64_t M, void* scratch, uint32_t* err, hipStream_t s,
+                               const uint16_t* q = nullptr, const uint16_t* k = nullptr,
+                               const int32_t* live_idx = nullptr, const int* m_live = nullptr);
+
 // number of compute units of the current device (cached)
 int cu_count();
 

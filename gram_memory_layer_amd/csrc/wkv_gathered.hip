@@ -59,7 +59,9 @@ __global__ void __launch_bounds__(256) prep_kernel(const int32_t* __restrict__ h
                                                    uint32_t* __restrict__ err,
                                                    const uint16_t* __restrict__ q,
                                                    const uint16_t* __restrict__ k,
-                                                   float* __restrict__ wqk, int nqk) {
+                                                   float* __restrict__ wqk, int nqk,
+                                                   const int32_t* __restrict__ live_idx,
+                                                   const int* __restrict__ m_live) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (wqk)
         for (int64_t j = i; j < nqk; j += (int64_t)gridDim.x * blockDim.x)
@@ -67,9 +69,19 @@ __global__ void __launch_bounds__(256) prep_kernel(const int32_t* __restrict__ h
     if (i >= (int64_t)n_cols * m_pad) return;
     const int c = (int)(i / m_pad);
     const int64_t m = i - (int64_t)c * m_pad;
+    // compacted rows: row r holds no position from the live count on
+    if (live_idx && m >= *m_live) {
+        aoff[i] = kBadRow;
+        scl[i] = make_float2(0.0f, 0.0f);
+    }
     uint32_t off = kBadRow;
     float2 sc = make_float2(0.0f, 0.0f);
+    int64_t r = m;  // the projection row of position m
     if (m < M) {
+        if (live_idx) {
+            r = live_idx[m];
+            if (r < 0) return;  // masked: not projected, its row never read
+        }
         const int32_t id = hash_ids[m * n_cols + c];
         if (id >= 0 && id < num_rows) {
             off = (uint32_t)id * 64u;
@@ -78,9 +90,11 @@ __global__ void __launch_bounds__(256) prep_kernel(const int32_t* __restrict__ h
         } else if (err) {
             atomicOr(err, ENGRAM_ERRBIT_ROW);
         }
+    } else if (live_idx) {
+        return;  // (padding rows are filled above, as rows past the live count)
     }
-    aoff[i] = off;
-    scl[i] = sc;
+    aoff[(int64_t)c * m_pad + r] = off;
+    scl[(int64_t)c * m_pad + r] = sc;
 }
 
 // Ring hand-over: wait until at most N of this wave's vector loads are in
@@ -723,11 +737,12 @@ hipError_t run_persistent(const uint32_t* aoff, const float2* scl, int n_cols, i
 hipError_t launch_prep(const Geom& g, const int32_t* hash_ids, const uint8_t* scales, int64_t M,
                        int64_t m_pad, uint32_t* aoff, float2* scl, uint32_t* err, hipStream_t s,
                        const uint16_t* q = nullptr, const uint16_t* k = nullptr,
-                       float* wqk = nullptr) {
+                       float* wqk = nullptr, const int32_t* live_idx = nullptr,
+                       const int* m_live = nullptr) {
     const int64_t total = (int64_t)g.n_cols * m_pad;
     prep_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s>>>(
         hash_ids, g.n_cols, M, m_pad, scales, g.num_embeddings, aoff, scl, err, q, k, wqk,
-        g.hc * g.dim);
+        g.hc * g.dim, live_idx, m_live);
     return hipGetLastError();
 }
 
@@ -782,6 +797,16 @@ GatheredScratch gathered_scratch(const Geom& g, int64_t M, void* base) {
     r.scl = reinterpret_cast<float2*>(r.aoff + (int64_t)g.n_cols * r.m_pad);
     r.wqk = reinterpret_cast<float*>(r.scl + (int64_t)g.n_cols * r.m_pad);
     return r;
+}
+
+hipError_t launch_prep_scratch(const Geom& g, const int32_t* hash_ids, const uint8_t* scales,
+                               int64_t M, void* scratch, uint32_t* err, hipStream_t s,
+                               const uint16_t* q, const uint16_t* k, const int32_t* live_idx,
+                               const int* m_live) {
+    if (M == 0) return hipSuccess;
+    const GatheredScratch gs = gathered_scratch(g, M, scratch);
+    return launch_prep(g, hash_ids, scales, M, gs.m_pad, gs.aoff, gs.scl, err, s, q, k,
+                       q ? gs.wqk : nullptr, live_idx, m_live);
 }
 
 hipError_t launch_wkv_gathered(const Geom& g, const int32_t* hash_ids, const uint8_t* table,

@@ -233,6 +233,23 @@ engram_status engram_forward(const engram_geometry* g, const engram_hash_tables*
                              void* workspace, size_t workspace_bytes, uint32_t* err,
                              void* stream);
 
+/* The forward from given hash ids, as [block] Engram.forward takes them
+ * (x, hash_ids, token_mask): stages 2 -> 3 -> 4 with the same paths as
+ * engram_forward (hash ids computed once for several layers by
+ * engram_hash_layers can be fed to each layer's call).
+ *   hash_ids int32 [n_tok, n_hash_cols]; x, out [n_tok, hc_mult, dim];
+ *   mask uint8 [n_tok] or NULL; gate fp32 [n_tok, hc_mult] or NULL.
+ * A hash id outside [0, num_embeddings) reads a zero row and sets
+ * ENGRAM_ERRBIT_ROW (for a projected position).  The workspace is sized by
+ * engram_forward_workspace_size.  Every output equals engram_forward's for
+ * the ids engram_hash gives. */
+engram_status engram_forward_hashed(const engram_geometry* g, const uint8_t* table,
+                                    const uint8_t* scales, const uint16_t* w, const uint16_t* q,
+                                    const uint16_t* k, const uint16_t* x,
+                                    const int32_t* hash_ids, const uint8_t* mask, int64_t n_tok,
+                                    uint16_t* out, float* gate, void* workspace,
+                                    size_t workspace_bytes, uint32_t* err, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

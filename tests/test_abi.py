@@ -115,6 +115,22 @@ def test_hash_layers_host_checks():
     assert call(B=0) == 0                                 # empty work: a no-op success
 
 
+def test_forward_hashed_host_checks():
+    lib = ge.load()
+    g = good()
+    fake = C.c_void_p(1 << 20)
+
+    def call(hid=fake, n=8, ws=fake, nbytes=1 << 40, x=fake):
+        return lib.engram_forward_hashed(C.byref(g), fake, fake, fake, fake, fake, x, hid, None,
+                                         n, fake, None, ws, nbytes, None, None)
+    assert call(n=-1) == 1
+    assert call(hid=None) == 1
+    assert call(x=C.c_void_p((1 << 20) + 2)) == 1          # x must be 16-byte aligned
+    assert call(ws=None) == 3
+    assert call(nbytes=100) == 3
+    assert call(n=0) == 0
+
+
 def test_fused_projection_host_checks():
     lib = ge.load()
     g = good()

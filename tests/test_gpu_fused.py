@@ -384,3 +384,43 @@ def test_forward_masked_compaction(ge, dev, kind, T, layout):
     assert torch.equal(out_a.reshape(T, -1)[mk].view(torch.int16),
                        x.reshape(T, -1)[mk].view(torch.int16))
     assert torch.all(gate_a.reshape(T, -1)[mk] == 0).item()
+
+
+# ------------------------------------------------------------------ forward from hash ids
+# The block's own signature (x, hash_ids, token_mask): the same outputs, bit
+# for bit, as the forward from token ids, on every path (64-wide fused tiles,
+# gather + projection, 256-wide fused tiles, fully fused with and without a
+# mask); and two layers hashed in one launch, then each layer's forward from
+# its block of ids, equal to each layer's forward from token ids.
+@pytest.mark.parametrize("shape,T,masked", [((256, 3, 3, 2), 37, True), ((256, 3, 3, 2), 300, True),
+                                            ((256, 3, 3, 2), 1100, False),
+                                            ((2048, 4, 3, 3), 4096, False),
+                                            ((2048, 4, 3, 3), 4096, True)])
+def test_forward_hashed_equals_forward(ge, dev, shape, T, masked):
+    dim, hc, mx, nh = shape
+    say("forward from hash ids", shape, T, masked)
+    layers = []
+    for l in range(2):
+        cfg = dataclasses.replace(synth.config("tiny"), dim=dim, hc_mult=hc, max_ngram_size=mx,
+                                  n_heads=nh, head_dim=64, scale_codes=(120, 132), index=300 + l)
+        layers.append(Workload(ge, cfg, dev))
+    cfg = layers[0].cfg
+    ids = torch.from_numpy(synth.token_ids(cfg, 1, T, name="fh")).to(dev)
+    x = synth.activations(cfg, T, dev, name="fhx").reshape(1, T, hc, dim)
+    mask = None
+    if masked:
+        mask = torch.from_numpy(synth.token_ids(cfg, 1, T, name="fhm") % 3 != 0).to(dev)
+    hid_all = ge.engram_hash_layers([w.g for w in layers], [w.tables for w in layers], ids)
+    for l, wl in enumerate(layers):
+        gate_a = torch.empty((1, T, hc), dtype=torch.float32, device=dev)
+        gate_b = torch.empty_like(gate_a)
+        err_a = torch.zeros(1, dtype=torch.int32, device=dev)
+        err_b = torch.zeros(1, dtype=torch.int32, device=dev)
+        out_a = ge.engram_forward(wl.g, wl.tables, wl.table, wl.scales, wl.w, wl.q, wl.k, x, ids,
+                                  mask=mask, gate=gate_a, err=err_a)
+        out_b = ge.engram_forward_hashed(wl.g, wl.table, wl.scales, wl.w, wl.q, wl.k, x,
+                                         hid_all[l], mask=mask, gate=gate_b, err=err_b)
+        torch.cuda.synchronize()
+        assert int(err_a.item()) == int(err_b.item()) == 0
+        assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16)), l
+        assert torch.equal(gate_a, gate_b), l
