@@ -38,6 +38,37 @@ engram_status from_hip(hipError_t e) { return e == hipSuccess ? ENGRAM_OK : ENGR
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// The forward's workspace, in order: hash ids; gathered rows or the fused
+// projection's scratch (whichever is larger); kv (or v and the partial
+// sums); the live-position maps.  engram_forward_workspace_size adds these up.
+struct FwdWorkspace {
+    int32_t* hash_ids;
+    uint16_t* rows;
+    uint16_t* kv;
+    int32_t* live_idx;
+    int32_t* rowmap;
+    int* m_live;
+};
+
+FwdWorkspace carve(const Geom& gg, int64_t n_tok, void* workspace) {
+    FwdWorkspace f;
+    char* ws = (char*)workspace;
+    f.hash_ids = (int32_t*)ws;
+    ws += align256((size_t)n_tok * gg.n_cols * sizeof(int32_t));
+    f.rows = (uint16_t*)ws;
+    const size_t rb = (size_t)n_tok * gg.K * sizeof(uint16_t);
+    const size_t sb = engram::gathered_scratch_bytes(gg, n_tok);
+    ws += align256(rb > sb ? rb : sb);
+    f.kv = (uint16_t*)ws;
+    ws += align256((size_t)n_tok * gg.N * sizeof(uint16_t));
+    f.live_idx = (int32_t*)ws;
+    ws += align256((size_t)n_tok * sizeof(int32_t));
+    f.rowmap = (int32_t*)ws;
+    ws += align256((size_t)engram::padded_rows(n_tok) * sizeof(int32_t));
+    f.m_live = (int*)ws;
+    return f;
+}
+
 }  // namespace
 
 extern "C" {
@@ -268,22 +299,13 @@ engram_status engram_forward(const engram_geometry* g, const engram_hash_tables*
     if (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
         return ENGRAM_ERR_WORKSPACE;
     const Geom gg = engram::make_geom(*g);
-    char* ws = (char*)workspace;
-    int32_t* hash_ids = (int32_t*)ws;
-    ws += align256((size_t)n_tok * gg.n_cols * sizeof(int32_t));
-    uint16_t* rows = (uint16_t*)ws;  // or the fused projection's scratch
-    {
-        const size_t rb = (size_t)n_tok * gg.K * sizeof(uint16_t);
-        const size_t sb = engram::gathered_scratch_bytes(gg, n_tok);
-        ws += align256(rb > sb ? rb : sb);
-    }
-    uint16_t* kv = (uint16_t*)ws;
-    ws += align256((size_t)n_tok * gg.N * sizeof(uint16_t));
-    int32_t* live_idx = (int32_t*)ws;
-    ws += align256((size_t)n_tok * sizeof(int32_t));
-    int32_t* rowmap = (int32_t*)ws;
-    ws += align256((size_t)engram::padded_rows(n_tok) * sizeof(int32_t));
-    int* m_live = (int*)ws;
+    const FwdWorkspace f = carve(gg, n_tok, workspace);
+    int32_t* hash_ids = f.hash_ids;
+    uint16_t* rows = f.rows;  // or the fused projection's scratch
+    uint16_t* kv = f.kv;
+    int32_t* live_idx = f.live_idx;
+    int32_t* rowmap = f.rowmap;
+    int* m_live = f.m_live;
     hipStream_t s = (hipStream_t)stream;
     // the fused gather + projection where its layout applies: 256-wide tiles
     // for prefill-sized batches, 64-wide ones for decode-sized batches;
@@ -350,22 +372,13 @@ engram_status engram_forward_hashed(const engram_geometry* g, const uint8_t* tab
     if (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
         return ENGRAM_ERR_WORKSPACE;
     const Geom gg = engram::make_geom(*g);
-    // the same workspace layout as engram_forward (its hash-id region unused)
-    char* ws = (char*)workspace;
-    ws += align256((size_t)n_tok * gg.n_cols * sizeof(int32_t));
-    uint16_t* rows = (uint16_t*)ws;
-    {
-        const size_t rb = (size_t)n_tok * gg.K * sizeof(uint16_t);
-        const size_t sb = engram::gathered_scratch_bytes(gg, n_tok);
-        ws += align256(rb > sb ? rb : sb);
-    }
-    uint16_t* kv = (uint16_t*)ws;
-    ws += align256((size_t)n_tok * gg.N * sizeof(uint16_t));
-    int32_t* live_idx = (int32_t*)ws;
-    ws += align256((size_t)n_tok * sizeof(int32_t));
-    int32_t* rowmap = (int32_t*)ws;
-    ws += align256((size_t)engram::padded_rows(n_tok) * sizeof(int32_t));
-    int* m_live = (int*)ws;
+    // the same workspace as engram_forward (its hash-id region unused)
+    const FwdWorkspace f = carve(gg, n_tok, workspace);
+    uint16_t* rows = f.rows;
+    uint16_t* kv = f.kv;
+    int32_t* live_idx = f.live_idx;
+    int32_t* rowmap = f.rowmap;
+    int* m_live = f.m_live;
     hipStream_t s = (hipStream_t)stream;
     const bool fused = (n_tok >= 1024 || n_tok <= 256) && aligned16(table) &&
                        engram::gathered_supported(gg, n_tok);
