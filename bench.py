@@ -167,6 +167,64 @@ def traffic_record(launch_flops_tokens: int):
     return rec.get("hbm_bytes_per_launch")
 
 
+def mfma_ceiling(dev, stream) -> dict:
+    """The part's matrix-core ceiling on this machine: the projection's MFMA back
+    to back from registers (libengram_probe.so), 8 waves per CU, once with
+    operands whose bits change every step (as in a GEMM) and once with zero
+    operands; TFLOP/s over event time, and the shader clock the loop ran at
+    (shader-clock ticks over constant-rate wall-clock ticks, median over
+    workgroups)."""
+    import ctypes as C
+    import torch
+    path = os.path.join(ROOT, "gram_memory_layer_amd", "libengram_probe.so")
+    if not os.path.exists(path):
+        raise SystemExit("libengram_probe.so is not built; run `python -m gram_memory_layer_amd.build`")
+    L = C.CDLL(path)
+    L.engram_probe_mfma_flops.restype = C.c_double
+    L.engram_probe_mfma_flops.argtypes = [C.c_int, C.c_int]
+    L.engram_probe_mfma.restype = C.c_int
+    L.engram_probe_mfma.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int,
+                                    C.c_void_p]
+    L.engram_probe_wall_clock_hz.restype = C.c_int
+    L.engram_probe_wall_clock_hz.argtypes = [C.POINTER(C.c_int64)]
+    hz = C.c_int64(0)
+    if L.engram_probe_wall_clock_hz(C.byref(hz)) != 0 or hz.value <= 0:
+        raise SystemExit("no wall-clock rate for the MFMA probe")
+    blocks = torch.cuda.get_device_properties(dev).multi_processor_count
+    threads = blocks * 512
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20262)
+    seed = torch.randint(-2**31, 2**31 - 1, (threads * 8,), dtype=torch.int32, device=dev,
+                         generator=gen)
+    sums = torch.empty(threads, dtype=torch.float32, device=dev)
+    clocks = torch.empty(blocks * 2, dtype=torch.int64, device=dev)
+    iters = 40000
+    res = {}
+    for mode, zero in (("changing_operands", 0), ("zero_operands", 1)):
+        def once():
+            r = L.engram_probe_mfma(seed.data_ptr(), sums.data_ptr(), clocks.data_ptr(), blocks,
+                                    iters, zero, stream.cuda_stream)
+            if r != 0:
+                raise SystemExit("MFMA probe launch failed: %d" % r)
+        once()
+        times = []
+        ratios = []
+        for _ in range(3):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            once()
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1) / 1e3)
+            c = clocks.cpu().view(-1, 2).double()
+            ratios.append(float((c[:, 0] / c[:, 1]).median()) * hz.value / 1e9)
+        t = sorted(times)[1]
+        res[mode] = {"tflops": round(L.engram_probe_mfma_flops(blocks, iters) / t / 1e12, 1),
+                     "clock_ghz": round(sorted(ratios)[1], 3)}
+    return res
+
+
 def time_launches(fn, n, stream):
     import torch
     start = torch.cuda.Event(enable_timing=True)
@@ -470,6 +528,12 @@ def main():
         torch.cuda.synchronize()
         rec["copy_calibration_bytes"] = 1 << 30
         del src, dst
+
+    # the same projection against the part's measured matrix-core ceiling
+    ceil = mfma_ceiling(dev, stream)
+    ceil["projection_frac_of_changing_operand_ceiling"] = round(
+        achieved / ceil["changing_operands"]["tflops"], 4)
+    rec["mfma_ceiling"] = ceil
 
     if not args.no_cpu_baseline:
         if args.cpu_threads > 0:

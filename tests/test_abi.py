@@ -27,6 +27,24 @@ def test_library_exports_every_declared_function():
         assert hasattr(lib, n), n
 
 
+def test_probe_library_loads_and_refuses_bad_arguments():
+    # the bench's MFMA ceiling probe: a library of its own, no Engram symbols
+    import ctypes as C
+    import os
+    path = os.path.join(os.path.dirname(ge.__file__), "libengram_probe.so")
+    lib = C.CDLL(path)
+    for n in ("engram_probe_mfma", "engram_probe_mfma_flops", "engram_probe_wall_clock_hz"):
+        assert hasattr(lib, n), n
+    assert not hasattr(lib, "engram_forward")
+    lib.engram_probe_mfma_flops.restype = C.c_double
+    lib.engram_probe_mfma_flops.argtypes = [C.c_int, C.c_int]
+    # 2 blocks x 8 waves x 10 steps x 8 MFMAs x 2*32*32*16 flop
+    assert lib.engram_probe_mfma_flops(2, 10) == 2 * 8 * 10 * 8 * 2 * 32 * 32 * 16
+    lib.engram_probe_mfma.restype = C.c_int
+    lib.engram_probe_mfma.argtypes = [C.c_void_p] * 3 + [C.c_int] * 3 + [C.c_void_p]
+    assert lib.engram_probe_mfma(None, None, None, 1, 1, 0, None) != 0   # nothing launched
+
+
 def good():
     return ge.Geometry.make(dim=5120, hc_mult=4, max_ngram_size=3, n_heads=12, head_dim=64,
                             num_embeddings=25160950, vocab=129280)
