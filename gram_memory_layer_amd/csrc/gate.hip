@@ -89,8 +89,9 @@ __global__ void __launch_bounds__(1024) gate_kernel(
     uint4 xr[HS][KC];
     if (!live) {
         // masked position: the gate is 0 and x passes through unchanged
+        // (nothing to move when out is x)
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) {
+        for (int i = 0; i < NCH && ot != xt; ++i) {
             const int c = tid + i * nthr;
             if (c < d8)
 #pragma unroll

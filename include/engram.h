@@ -170,7 +170,8 @@ engram_status engram_wkv_gathered(const engram_geometry* g, const uint8_t* table
  *   out = bf16(h + g*value); a masked position returns x bit-exactly.
  *   x    bf16 [n_tok, hc_mult, dim];  kv bf16 [n_tok, dim*(hc_mult+1)];
  *   q, k bf16 [hc_mult, dim];  mask uint8 [n_tok] or NULL (all live);
- *   out  bf16 [n_tok, hc_mult, dim] (may be the same buffer as x);
+ *   out  bf16 [n_tok, hc_mult, dim] (may be the same buffer as x: then a
+ *        masked position is not touched at all);
  *   gate fp32 [n_tok, hc_mult] or NULL.
  * fp32 arithmetic with fixed-order reductions (run-to-run deterministic). */
 engram_status engram_gate_add(const engram_geometry* g, const uint16_t* x, const uint16_t* kv,
