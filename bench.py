@@ -705,6 +705,12 @@ def long_mixed(args):
         lambda: ge.engram_wkv_gate_partials(g, table, scales, hid_l, w, x_l, q, k, v=v_l,
                                             part=part_l), steps, stream)
     achieved = 2 * g.K * g.N * n_live / sec_proj / 1e12
+    # the row gather on its own over every position (Zipf ids: rows repeat)
+    rows = ge.engram_gather(g, table, scales, hid)
+    sec_gather = time_launches(lambda: ge.engram_gather(g, table, scales, hid, rows=rows), steps,
+                               stream)
+    gather_read = n_tok * g.n_hash_cols * (g.head_dim + g.head_dim // 32)
+    gather_write = n_tok * g.K * 2
     # the forward with out aliasing x (a masked position is then not touched);
     # on a copy of x, which it overwrites
     xi = x.clone()
@@ -729,6 +735,13 @@ def long_mixed(args):
         "live_positions": n_live,
         "dense_stage_calls_ms": round(sec_dense * 1e3, 4),
         "out_aliasing_x_ms": round(sec_inplace * 1e3, 4),
+        "gather_hbm": {"kernel": "engram_gather (every position)",
+                       "achieved": round((gather_read + gather_write) / sec_gather / 1e9, 1),
+                       "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                       "frac": round((gather_read + gather_write) / sec_gather / 1e9 /
+                                     PEAK_HBM_GBS, 4),
+                       "read_bytes": gather_read, "write_bytes": gather_write,
+                       "us": round(sec_gather * 1e6, 2)},
         "live_projection_ms": round(sec_proj * 1e3, 4),
         "wall_s": round(wall, 3),
     }
