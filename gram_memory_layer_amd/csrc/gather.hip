@@ -5,12 +5,15 @@
 // table row plus that 32-block's scale byte and writes 16 bytes of bf16.
 // Eight consecutive threads cover one 64-byte table row and one 128-byte
 // output row, and consecutive rows (hash columns of a position) are adjacent
-// in the output, so stores are fully coalesced.  The table reads are random
-// 64-byte rows by construction.
+// in the output, so stores are fully coalesced (nontemporal: 2% faster at
+// the T=32,768 shape).  The table reads are random 64-byte rows by
+// construction.
 #include "dequant.h"
 
 namespace engram {
 namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __global__ void __launch_bounds__(256) gather_kernel(const uint8_t* __restrict__ table,
                                                      const uint8_t* __restrict__ scales,
@@ -36,7 +39,8 @@ __global__ void __launch_bounds__(256) gather_kernel(const uint8_t* __restrict__
         dequant8(codes.x, codes.y, sc, p);
         o = make_uint4(p[0], p[1], p[2], p[3]);
     }
-    *reinterpret_cast<uint4*>(rows + r * head_dim + j0) = o;
+    const u32x4 u = {o.x, o.y, o.z, o.w};  // written once: nontemporal hint
+    __builtin_nontemporal_store(u, reinterpret_cast<u32x4*>(rows + r * head_dim + j0));
 }
 
 }  // namespace
