@@ -1,6 +1,7 @@
 // fp8 e4m3fn value times an e8m0 power-of-two scale, rounded to bf16
-// ("Module engram" docs, stage 2 / regen_table: values.float() * scales.float()
-// per 32-block, then bf16).
+// ("Module engram" docs, stage 2 and regen_table: each value is widened to
+// fp32, multiplied by the scale of its 32-wide block, and the product is
+// rounded to bf16).
 //
 // The e4m3 code is decoded by bit manipulation (exact in fp32: 1 sign,
 // 4 exponent bits with bias 7, 3 fraction bits, exponent field 0 subnormal,

@@ -21,8 +21,8 @@
  * Precision: every floating-point step is evaluated in fp64 and rounded once
  * to the output format (bf16 for rows, kv and out; fp32 for the gate).  The
  * one place the definition itself rounds in between -- the dequantising
- * product "values.float() * scales.float(), then bf16" -- is rounded to fp32
- * first and then to bf16, exactly as written.
+ * product, which the docs (regen_table) form in fp32 and only then round to
+ * bf16 -- is rounded to fp32 first and then to bf16, in that order.
  *
  * Parity status: every function here is pinned by the CPU tests (closed
  * forms, special cases, library cross-checks, brute force); none is
@@ -284,8 +284,9 @@ void eo_linear(int64_t M, int64_t N, int64_t K, const uint16_t* a, const uint16_
  *   g     = sigmoid( copysign( sqrt(max(|a|, clamp)), a ) ),  clamp = fp32(1e-6)
  *   g     = 0 where token_mask is False
  *   out   = bf16(h + g * value)
- * All in fp64.  A masked position returns x unchanged (the docs and the gate
- * page: such positions pass through untouched).  gate_out [tokens, hc] gets g
+ * All in fp64.  A masked position returns x unchanged (the block's forward
+ * docstring says a False mask leaves the position as it was; the gate page
+ * gives image positions a zero gate).  gate_out [tokens, hc] gets g
  * rounded to fp32 and a_out [tokens, hc] the fp64 a (either may be NULL).
  * mask may be NULL (every position live). */
 void eo_gate_and_add(int64_t n_tok, int hc, int dim, float eps, const uint16_t* x,

@@ -2,10 +2,13 @@
 benchmark times.
 
 Integer stages are compared everywhere (hash ids for every position, the row
-gather for every position); floating-point outputs on sampled positions that
-the oracle computes one by one (sampled rows of the projection, sampled
-tokens end to end), plus properties that hold at any size (masked positions
-return x bit-exactly, exactly orthogonal keys give sigmoid(+sqrt(1e-6))).
+gather for every position).  Floating-point outputs: at the T=4096 prefill
+every element of the projection and every position's gate and output; at
+the other workloads, positions the oracle computes one by one (every
+sequence of the checked decode steps, four live positions of every projected
+tile of the long mixed prefill), plus properties that hold at any size
+(masked positions return x bit-exactly, exactly orthogonal keys give
+sigmoid(+sqrt(1e-6)), the same call twice gives the same bits).
 """
 import numpy as np
 import pytest
@@ -51,27 +54,30 @@ def _oracle_tokens(wl, ids_row, positions, x_bits, mask_bits=None):
     return dict(hash_ids=hid, rows=rows, kv=kv, out=out, gate=gate, a=a)
 
 
-def _check_tokens(ref, out_bits, gate_gpu, x_bits, cfg):
-    hd = cfg.hc_mult * cfg.dim
-    n = x_bits.shape[0]
-    da = tolerances.key_ulp_da(x_bits, ref["kv"][:, :hd].reshape(n, cfg.hc_mult, cfg.dim),
-                               bits_q(ref), bits_k(ref), cfg.norm_eps)
-    gs = tolerances.check_gate(gate_gpu, ref["gate"], ref["a"], da=da)
-    os_ = tolerances.check_out(out_bits, ref["out"], x_bits, ref["kv"][:, hd:], gate_gpu,
-                               ref["gate"], v_ulps=1)
-    return gs, os_
-
-
-def bits_q(ref):
-    return ref["_q"]
-
-
-def bits_k(ref):
-    return ref["_k"]
+def _check_tokens(ref, out_bits, gate_gpu, x_bits, wl, min_tight, max_rel, max_frac_beyond):
+    """End-to-end check of sampled or all positions (tolerances.check_end_to_end)."""
+    cfg = wl.cfg
+    return tolerances.check_end_to_end(out_bits, gate_gpu, x_bits, ref, ref["rows"], bits(wl.w),
+                                       bits(wl.q), bits(wl.k), cfg.norm_eps, min_tight=min_tight,
+                                       max_rel=max_rel, max_frac_beyond=max_frac_beyond)
 
 
 # ------------------------------------------------------------------ T=4096 prefill
+# Floors on the observed rates (each workload's measured value in the
+# comment).  Margins: a fraction of gates within 1e-5 at least 0.05 under
+# the observed one (0.1 where fewer than 100 gates are checked), ceilings
+# about 3x the observed fraction of outputs beyond 2 ulp and of kv elements
+# beyond 1 ulp, and 5x the observed largest relative gate difference.
+# T=4096 prefill, every position: kv 0.99987 bit-equal, 712 of 104.9M
+# elements beyond 1 ulp (all within 0.013 of their cancellation bound);
+# gates 0.946 within 1e-5, largest difference 2.24e-4; outputs 5.6e-5
+# beyond 2 ulp.
+PREFILL_FLOORS = dict(kv_bit_equal=0.9998, kv_beyond_1ulp=2000, gate_tight=0.89,
+                      gate_max_rel=1.1e-3, out_beyond_2ulp=1.7e-4)
+
+
 def test_prefill_full(ge, dev):
+    import time
     say("prefill full: building 25.16M-row table")
     wl = Workload(ge, "prefill", dev)
     cfg = wl.cfg
@@ -79,13 +85,20 @@ def test_prefill_full(ge, dev):
     ids_np = synth.token_ids(cfg, B, T)
     ids = torch.from_numpy(ids_np).to(dev)
     x = synth.activations(cfg, B * T, dev).reshape(B, T, cfg.hc_mult, cfg.dim)
-    state = torch.full((B, cfg.max_ngram_size - 1), cfg.pad_id, dtype=torch.int32, device=dev)
-    gate = torch.empty((B, T, cfg.hc_mult), dtype=torch.float32, device=dev)
-    err = torch.zeros(1, dtype=torch.int32, device=dev)
     layer = ge.EngramLayer(wl.g, wl.tables, wl.table, wl.scales, wl.w, wl.q, wl.k)
-    out = layer.forward(x, ids, state=state, gate=gate, err=err)
-    torch.cuda.synchronize()
-    assert int(err.item()) == 0
+    runs = []
+    for rep in range(2):  # the same forward twice: every output bit for bit
+        state = torch.full((B, cfg.max_ngram_size - 1), cfg.pad_id, dtype=torch.int32,
+                           device=dev)
+        gate = torch.empty((B, T, cfg.hc_mult), dtype=torch.float32, device=dev)
+        err = torch.zeros(1, dtype=torch.int32, device=dev)
+        out = layer.forward(x, ids, state=state, gate=gate, err=err)
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
+        runs.append((out, gate, state))
+    (out, gate, state), (out2, gate2, state2) = runs
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(gate, gate2) and torch.equal(state, state2)
     say("prefill full: hash and gather for every position")
     ref_hid = oracle.hash_ids(wl.t, wl.geom, oracle.HashState(B, T + 4), ids_np)
     hid = ge.engram_hash(wl.g, wl.tables, ids)
@@ -96,21 +109,35 @@ def test_prefill_full(ge, dev):
     rows = ge.engram_gather(wl.g, wl.table, wl.scales, torch.from_numpy(ref_hid).to(dev))
     assert np.array_equal(bits(rows).reshape(ref_rows.shape), ref_rows)
 
-    say("prefill full: projection, sampled rows of the full M=4096 launch")
-    kv = ge.engram_wkv(wl.g, rows, wl.w)
-    pos = _sample_positions(T, n=12, seed=1)
-    ref_kv = oracle.linear(ref_rows[pos], bits(wl.w))
-    absdot = np.abs(tolerances.bf16_value(ref_rows[pos])) @ np.abs(tolerances.bf16_value(bits(wl.w))).T
-    st = tolerances.check_kv(bits(kv[torch.from_numpy(pos).to(dev)]), ref_kv, absdot, wl.g.K)
-    say("   kv", st)
+    say("prefill full: oracle projection of all %d positions (%d threads)" % (
+        B * T, oracle.num_threads()))
+    t0 = time.time()
+    ref_kv = oracle.linear(ref_rows, bits(wl.w))
+    say("   oracle projection %.1f s" % (time.time() - t0))
+    wabs = np.abs(tolerances.bf16_value(bits(wl.w)))
+    absdot = lambda r: np.abs(tolerances.bf16_value(ref_rows[r])) @ wabs.T
+    # both projections the forward can run, every element: the fused gather
+    # (the forward's kernel without the gate epilogue) and the bf16 one
+    for name, kv in (("wkv_gathered", ge.engram_wkv_gathered(wl.g, wl.table, wl.scales,
+                                                              torch.from_numpy(ref_hid).to(dev),
+                                                              wl.w)),
+                     ("wkv", ge.engram_wkv(wl.g, rows, wl.w))):
+        st = tolerances.check_kv(bits(kv), ref_kv, absdot, wl.g.K,
+                                 min_equal=PREFILL_FLOORS["kv_bit_equal"],
+                                 max_beyond=PREFILL_FLOORS["kv_beyond_1ulp"])
+        say("   kv", name, st)
+        del kv
 
-    say("prefill full: end to end on sampled positions")
+    say("prefill full: end to end, every position")
     xb = bits(x).reshape(B * T, cfg.hc_mult, cfg.dim)
-    ref = _oracle_tokens(wl, ids_np[0], pos, xb[pos])
-    ref["_q"], ref["_k"] = bits(wl.q), bits(wl.k)
-    gs, os_ = _check_tokens(ref, bits(out).reshape(B * T, cfg.hc_mult, cfg.dim)[pos],
-                            gate.cpu().numpy().reshape(B * T, -1)[pos], xb[pos], cfg)
-    say("   gate", gs, "out", os_)
+    r_out, r_gate, r_a = oracle.gate_and_add(xb, ref_kv, bits(wl.q), bits(wl.k), cfg.norm_eps)
+    ref = dict(rows=ref_rows, kv=ref_kv, out=r_out, gate=r_gate, a=r_a)
+    st = _check_tokens(ref, bits(out).reshape(B * T, cfg.hc_mult, cfg.dim),
+                       gate.cpu().numpy().reshape(B * T, -1), xb, wl,
+                       min_tight=PREFILL_FLOORS["gate_tight"],
+                       max_rel=PREFILL_FLOORS["gate_max_rel"],
+                       max_frac_beyond=PREFILL_FLOORS["out_beyond_2ulp"])
+    say("   end to end", st)
 
 
 # ------------------------------------------------------------------ fully fused prefill
@@ -137,10 +164,12 @@ def test_forward_gate_partials_geometry(ge, dev, dim, n_heads, T, inplace):
     pos = _sample_positions(T, extra=(255, 256, T - 257, T - 256), n=10, seed=T)
     mk = mask_np.reshape(-1)
     ref = _oracle_tokens(wl, ids_np[0], pos, xb[pos], mk[pos])
-    ref["_q"], ref["_k"] = bits(wl.q), bits(wl.k)
-    gs, os_ = _check_tokens(ref, bits(out).reshape(T, cfg.hc_mult, cfg.dim)[pos],
-                            gate.cpu().numpy().reshape(T, -1)[pos], xb[pos], cfg)
-    say("   gate", gs, "out", os_)
+    # observed: every gate within 1e-5 (largest difference 8.3e-6), at most
+    # 6.8e-6 of outputs beyond 2 ulp; the sample holds 60-70 gates
+    st = _check_tokens(ref, bits(out).reshape(T, cfg.hc_mult, cfg.dim)[pos],
+                       gate.cpu().numpy().reshape(T, -1)[pos], xb[pos], wl, min_tight=0.9,
+                       max_rel=4.2e-5, max_frac_beyond=1e-4)
+    say("   end to end", st)
     # masked positions pass x through bit for bit, with gate 0
     masked = np.nonzero(mk == 0)[0][:50]
     if len(masked):
@@ -172,6 +201,11 @@ def test_wkv_full_width_tail_split(ge, dev, M):
 
 
 # ------------------------------------------------------------------ decode after prefill
+# decode, all 64 sequences at 5 steps (256 gates each): lowest per-step rate
+# 0.923 within 1e-5, largest difference 8.1e-5, at most 5.6e-5 beyond 2 ulp
+DECODE_FLOORS = dict(gate_tight=0.87, gate_max_rel=4e-4, out_beyond_2ulp=1.7e-4)
+
+
 def test_decode_full(ge, dev):
     say("decode: building tables")
     wl = Workload(ge, "decode", dev)
@@ -186,7 +220,7 @@ def test_decode_full(ge, dev):
     assert np.array_equal(got_pre.cpu().numpy(), ref_pre)
     layer = ge.EngramLayer(wl.g, wl.tables, wl.table, wl.scales, wl.w, wl.q, wl.k)
     check_steps = {0, 1, 2, 63, S - 1}
-    rows_to_check = np.array([0, 17, 40, B - 1])
+    rows_to_check = np.arange(B)  # every sequence of a checked step
     for step in range(S):
         ids_s = steps[:, step:step + 1].copy()
         ids_t = torch.from_numpy(ids_s).to(dev)
@@ -206,9 +240,13 @@ def test_decode_full(ge, dev):
             kv = oracle.linear(rows, bits(wl.w))
             xb = bits(x).reshape(B, cfg.hc_mult, cfg.dim)[rows_to_check]
             r_out, r_gate, r_a = oracle.gate_and_add(xb, kv, bits(wl.q), bits(wl.k), cfg.norm_eps)
-            ref = dict(kv=kv, out=r_out, gate=r_gate, a=r_a, _q=bits(wl.q), _k=bits(wl.k))
-            _check_tokens(ref, bits(out).reshape(B, cfg.hc_mult, cfg.dim)[rows_to_check],
-                          gate.cpu().numpy().reshape(B, -1)[rows_to_check], xb, cfg)
+            ref = dict(rows=rows, kv=kv, out=r_out, gate=r_gate, a=r_a)
+            st = _check_tokens(ref, bits(out).reshape(B, cfg.hc_mult, cfg.dim)[rows_to_check],
+                               gate.cpu().numpy().reshape(B, -1)[rows_to_check], xb, wl,
+                               min_tight=DECODE_FLOORS["gate_tight"],
+                               max_rel=DECODE_FLOORS["gate_max_rel"],
+                               max_frac_beyond=DECODE_FLOORS["out_beyond_2ulp"])
+            say("   end to end", st)
     # after 512 + 128 tokens the state holds the last two compressed ids
     assert np.array_equal(state.cpu().numpy(), wl.t["token_map"][steps[:, -2:]])
 
@@ -353,11 +391,12 @@ def test_forward_largest_fused_prefill(ge, dev):
     pos = pos[mk[pos]]
     xb = bits(x.reshape(T, cfg.hc_mult, cfg.dim)[torch.from_numpy(pos).to(dev)])
     ref = _oracle_tokens(wl, ids_np[0], pos, xb, mk[pos])
-    ref["_q"], ref["_k"] = bits(wl.q), bits(wl.k)
     ob = bits(out.reshape(T, cfg.hc_mult, cfg.dim)[torch.from_numpy(pos).to(dev)])
-    gs, os_ = _check_tokens(ref, ob, gate.reshape(T, -1)[torch.from_numpy(pos).to(dev)].cpu().numpy(),
-                            xb, cfg)
-    say("   gate", gs, "out", os_)
+    # observed: 0.906 of 64 gates within 1e-5, largest difference 4.3e-5,
+    # 3.3e-5 of outputs beyond 2 ulp
+    st = _check_tokens(ref, ob, gate.reshape(T, -1)[torch.from_numpy(pos).to(dev)].cpu().numpy(),
+                       xb, wl, min_tight=0.8, max_rel=2.2e-4, max_frac_beyond=1e-4)
+    say("   end to end", st)
     m = torch.from_numpy(~mk).to(dev)
     assert torch.equal(out.reshape(T, -1)[m].view(torch.int16), x.reshape(T, -1)[m].view(torch.int16))
 
@@ -431,6 +470,11 @@ def test_gate_stress_full(ge, dev):
 
 
 # ------------------------------------------------------------------ long mixed prefill
+# long mixed, 365 live positions over the 88 projected tiles: 0.958 within
+# 1e-5, largest difference 1.66e-4, 5.6e-5 beyond 2 ulp
+LONG_MIXED_FLOORS = dict(gate_tight=0.90, gate_max_rel=8.3e-4, out_beyond_2ulp=1.7e-4)
+
+
 def test_long_mixed_full(ge, dev):
     say("long mixed: building tables")
     wl = Workload(ge, "long_mixed", dev)
@@ -442,10 +486,19 @@ def test_long_mixed_full(ge, dev):
     ids = torch.from_numpy(ids_np).to(dev)
     mask = torch.from_numpy(mask_np).to(dev)
     x = synth.activations(cfg, B * T, dev).reshape(B, T, cfg.hc_mult, cfg.dim)
-    gate = torch.empty((B, T, cfg.hc_mult), dtype=torch.float32, device=dev)
     layer = ge.EngramLayer(wl.g, wl.tables, wl.table, wl.scales, wl.w, wl.q, wl.k)
-    out = layer.forward(x, ids, mask=mask, gate=gate)
-    torch.cuda.synchronize()
+    runs = []
+    for rep in range(2):  # the same forward twice: every output bit for bit
+        state = torch.full((B, cfg.max_ngram_size - 1), cfg.pad_id, dtype=torch.int32,
+                           device=dev)
+        gate = torch.empty((B, T, cfg.hc_mult), dtype=torch.float32, device=dev)
+        out = layer.forward(x, ids, mask=mask, state=state, gate=gate)
+        torch.cuda.synchronize()
+        runs.append((out, gate, state))
+    (out, gate, state), (out2, gate2, state2) = runs
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(gate, gate2) and torch.equal(state, state2)
+    del out2, gate2
     say("long mixed: masked positions pass through")
     m = ~mask.reshape(-1)
     assert torch.equal(out.reshape(B * T, -1)[m].view(torch.int16),
@@ -455,19 +508,33 @@ def test_long_mixed_full(ge, dev):
     ref_hid = oracle.hash_ids(wl.t, wl.geom, oracle.HashState(B, T + 4), ids_np)
     hid = ge.engram_hash(wl.g, wl.tables, ids)
     assert np.array_equal(hid.cpu().numpy(), ref_hid)
+    assert np.array_equal(state.cpu().numpy(), wl.t["token_map"][ids_np[:, -2:]])
     tab, sc, inv = wl.host_rows(ref_hid)
     ref_rows = oracle.embed_rows(tab, sc, inv.reshape(-1)).reshape(B * T, -1)
     rows = ge.engram_gather(wl.g, wl.table, wl.scales, torch.from_numpy(ref_hid).to(dev))
     assert np.array_equal(bits(rows).reshape(ref_rows.shape), ref_rows)
-    say("long mixed: end to end on sampled positions (span edges included)")
+    del rows
+    # The forward packs the live positions in order and projects them in
+    # 256-row tiles: four live positions of every such tile (its first, its
+    # last and two at random), plus the span edges, end to end.
+    say("long mixed: end to end, four live positions per projected tile")
+    live = np.nonzero(mask_np[0])[0]
+    rng = np.random.default_rng(5)
+    pick = []
+    for t0 in range(0, len(live), 256):
+        t1 = min(len(live), t0 + 256)
+        pick += [t0, t1 - 1] + rng.integers(t0, t1, 2).tolist()
     edges = np.nonzero(np.diff(mask_np[0].astype(np.int8)))[0]
-    pos = _sample_positions(T, extra=list(edges[:6]) + list(edges[:6] + 1), n=12, seed=5)
+    pos = np.unique(np.concatenate([live[pick], edges[:8], edges[:8] + 1]))
+    say("   %d positions over %d tiles" % (len(pos), (len(live) + 255) // 256))
     xb = bits(x).reshape(B * T, cfg.hc_mult, cfg.dim)[pos]
     ref = _oracle_tokens(wl, ids_np[0], pos, xb, mask_np[0][pos])
-    ref["_q"], ref["_k"] = bits(wl.q), bits(wl.k)
-    gs, os_ = _check_tokens(ref, bits(out).reshape(B * T, cfg.hc_mult, cfg.dim)[pos],
-                            gate.cpu().numpy().reshape(B * T, -1)[pos], xb, cfg)
-    say("   gate", gs, "out", os_)
+    st = _check_tokens(ref, bits(out).reshape(B * T, cfg.hc_mult, cfg.dim)[pos],
+                       gate.cpu().numpy().reshape(B * T, -1)[pos], xb, wl,
+                       min_tight=LONG_MIXED_FLOORS["gate_tight"],
+                       max_rel=LONG_MIXED_FLOORS["gate_max_rel"],
+                       max_frac_beyond=LONG_MIXED_FLOORS["out_beyond_2ulp"])
+    say("   end to end", st)
 
 
 def test_empty_calls_launch_nothing(ge, dev):

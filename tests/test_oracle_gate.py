@@ -191,10 +191,15 @@ def test_output_is_one_rounding_of_h_plus_g_v():
     assert np.array_equal(out[:, 0], expect)
 
 
-def test_agrees_with_fp32_torch_forward_of_the_page():
-    # The Engram block's forward after the projection, run by torch on CPU in
-    # fp32 (its own summation order): a semantics cross-check (split order,
-    # sign convention, masking, cast), within fp32 tolerances.
+def test_agrees_with_fp32_torch_evaluation_of_the_gate_equations():
+    # A semantics cross-check of the oracle (which stream a key belongs to,
+    # the sign convention, the weight, masking, the final cast) against an
+    # independent fp32 evaluation in torch on the CPU, in its own summation
+    # order, of the "Gate per stream" page's two equations: a_k as the
+    # weighted dot of stream k with its key over the product of the two RMS
+    # values and sqrt(dim) (eps inside each RMS, as the block's code has it),
+    # and g as the sigmoid of the signed square root of |a_k| clamped at
+    # 1e-6.  The value is the last dim columns of kv, added to every stream.
     cfg = synth.config("tiny")
     g = torch.Generator().manual_seed(1)
     T, hc, D = 64, cfg.hc_mult, cfg.dim
@@ -202,22 +207,29 @@ def test_agrees_with_fp32_torch_forward_of_the_page():
     kv = torch.randn(T, D * (hc + 1), generator=g).to(torch.bfloat16)
     kv[:, :hc * D] += (x.float() * torch.rand(T, hc, 1, generator=g) * 2 - 1).reshape(T, -1).to(torch.bfloat16)
     q, k = synth.qk_weights(cfg, "cpu")
-    mask = torch.rand(T, generator=g) > 0.2
+    live = torch.rand(T, generator=g) > 0.2
     eps = cfg.norm_eps
-    key, value = kv.split([hc * D, D], dim=-1)
-    key = key.float().unflatten(-1, (hc, D))
-    weight = q.float() * k.float()
-    h = x.float()
-    rstd = torch.rsqrt(h.square().mean(-1) + eps) * torch.rsqrt(key.square().mean(-1) + eps)
-    dot = (h * weight * key).sum(-1) * rstd * D ** -0.5
-    gate_t = torch.sigmoid(torch.copysign(dot.abs().clamp_min(1e-6).sqrt(), dot))
-    gate_t = gate_t.masked_fill(~mask.unsqueeze(-1), 0)
-    out_t = (h + gate_t.unsqueeze(-1) * value.float().unsqueeze(-2)).to(torch.bfloat16)
+    X = x.float()
+    value = kv[:, hc * D:].float()
+    gate_t = torch.zeros(T, hc)
+    out_t = torch.empty(T, hc, D)
+    for s in range(hc):
+        keys = kv[:, s * D:(s + 1) * D].float()          # [T, D], stream s's key
+        wk = q[s].float() * k[s].float() * keys          # w_{k,f} * key_{k,f}
+        num = torch.linalg.vecdot(X[:, s], wk)           # sum over f
+        rms_x = torch.sqrt(torch.mean(X[:, s] ** 2, dim=1) + eps)
+        rms_k = torch.sqrt(torch.mean(keys ** 2, dim=1) + eps)
+        a_s = num / (rms_x * rms_k * math.sqrt(D))
+        root = torch.sqrt(torch.clamp(a_s.abs(), min=1e-6))
+        g_s = torch.sigmoid(torch.where(a_s < 0, -root, root))
+        gate_t[:, s] = torch.where(live, g_s, torch.zeros_like(g_s))
+        out_t[:, s] = X[:, s] + gate_t[:, s, None] * value
+    out_t = out_t.to(torch.bfloat16)
     b = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
-    out, gate, a = oracle.gate_and_add(b(x), b(kv), b(q), b(k), eps, mask.numpy())
+    out, gate, a = oracle.gate_and_add(b(x), b(kv), b(q), b(k), eps, live.numpy())
     tolerances.check_gate(gate_t.numpy(), gate, a)
-    tolerances.check_out(b(out_t), out, b(x), b(value), gate_t.numpy(), gate)
-    assert np.array_equal(out[~mask.numpy()], b(x)[~mask.numpy()])
+    tolerances.check_out(b(out_t), out, b(x), b(kv[:, hc * D:]), gate_t.numpy(), gate)
+    assert np.array_equal(out[~live.numpy()], b(x)[~live.numpy()])
 
 
 def test_page_counts():
