@@ -36,7 +36,9 @@ _LIB_PATH = os.path.join(_HERE, "libengram.so")
 
 ERRBIT_TOKEN, ERRBIT_HASH, ERRBIT_ROW = 0x1, 0x2, 0x4
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported geometry",
-           3: "workspace missing or too small", 4: "HIP runtime error"}
+           3: "workspace missing or too small", 4: "HIP runtime error",
+           5: "call needs more than the fixed scratch array holds"}
+ERR_TOO_LARGE = 5
 
 
 class EngramError(RuntimeError):
@@ -123,6 +125,10 @@ def load():
     L.engram_forward.restype = C.c_int
     L.engram_forward.argtypes = [G, HT, P, P, P, P, P, P, P, P, P, i32, i32, P, P, P, C.c_size_t,
                                  P, P]
+    L.engram_fixed_scratch_bytes.restype = C.c_size_t
+    L.engram_fixed_scratch_bytes.argtypes = []
+    L.engram_forward_noalloc.restype = C.c_int
+    L.engram_forward_noalloc.argtypes = [G, HT, P, P, P, P, P, P, P, P, P, i32, i32, P, P, P, P]
     _lib = L
     return L
 
@@ -476,6 +482,45 @@ def engram_forward_hashed(g: Geometry, table, scales, w, q, k, x, hash_ids, mask
         C.byref(g), table.data_ptr(), scales.data_ptr(), w.data_ptr(), q.data_ptr(), k.data_ptr(),
         x.data_ptr(), hash_ids.data_ptr(), _ptr(m), n_tok, out.data_ptr(), _ptr(gate),
         workspace.data_ptr(), workspace.numel(), _ptr(err), _stream(dev)))
+    return out
+
+
+def engram_fixed_scratch_bytes() -> int:
+    """Size of the library's fixed per-GPU scratch array (engram_forward_noalloc)."""
+    return int(load().engram_fixed_scratch_bytes())
+
+
+def engram_forward_noalloc(g: Geometry, tables: dict, table, scales, w, q, k, x, ids, out,
+                           mask=None, state=None, gate=None, err=None):
+    """engram_forward with the library's fixed scratch array as its workspace:
+    nothing is allocated by this call (out, and gate/err if wanted, are the
+    caller's).  Raises EngramError (ENGRAM_ERR_TOO_LARGE) when the call's
+    workspace would not fit the array."""
+    L = load()
+    dev = x.device
+    _dev(ids, "ids", torch.int32, None, dev)
+    if ids.dim() != 2:
+        raise ValueError("ids must be [B, T]")
+    B, T = ids.shape
+    _dev(x, "x", torch.bfloat16, (B, T, g.hc_mult, g.dim), dev)
+    ht = _tables(tables, g, dev)
+    _dev(table, "table", torch.uint8, (g.num_embeddings, g.head_dim), dev)
+    _dev(scales, "scales", torch.uint8, (g.num_embeddings, g.head_dim // 32), dev)
+    _dev(w, "w", torch.bfloat16, (g.N, g.K), dev)
+    _dev(q, "q", torch.bfloat16, (g.hc_mult, g.dim), dev)
+    _dev(k, "k", torch.bfloat16, (g.hc_mult, g.dim), dev)
+    if state is not None:
+        _dev(state, "state", torch.int32, (B, g.max_ngram_size - 1), dev)
+    m = _mask(mask, B * T, dev)
+    _dev(out, "out", torch.bfloat16, (B, T, g.hc_mult, g.dim), dev)
+    if gate is not None:
+        _dev(gate, "gate", torch.float32, (B, T, g.hc_mult), dev)
+    if err is not None:
+        _dev(err, "err", torch.int32, (1,), dev)
+    _check("engram_forward_noalloc", L.engram_forward_noalloc(
+        C.byref(g), C.byref(ht), table.data_ptr(), scales.data_ptr(), w.data_ptr(), q.data_ptr(),
+        k.data_ptr(), _ptr(state), x.data_ptr(), ids.data_ptr(), _ptr(m), B, T, out.data_ptr(),
+        _ptr(gate), _ptr(err), _stream(dev)))
     return out
 
 

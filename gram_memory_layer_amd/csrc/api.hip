@@ -71,6 +71,94 @@ FwdWorkspace carve(const Geom& gg, int64_t n_tok, void* workspace) {
 
 }  // namespace
 
+namespace engram {
+
+// Every argument check of engram_forward except the workspace's.
+engram_status forward_check(const engram_geometry* g, const engram_hash_tables* t,
+                            const uint8_t* table, const uint8_t* scales, const uint16_t* w,
+                            const uint16_t* q, const uint16_t* k, const uint16_t* x,
+                            const int32_t* ids, int32_t B, int32_t T, const uint16_t* out) {
+    engram_status st = engram_check_geometry(g);
+    if (st != ENGRAM_OK) return st;
+    if (t == nullptr || B < 0 || T < 0) return ENGRAM_ERR_INVALID_ARG;
+    const int64_t n_tok = (int64_t)B * T;
+    if (n_tok >= kMaxTokens) return ENGRAM_ERR_INVALID_ARG;
+    if (n_tok == 0) return ENGRAM_OK;
+    if (!t->token_map || !t->mult || !t->prime || !t->offset || !ids) return ENGRAM_ERR_INVALID_ARG;
+    if (!table || !scales || !w || !q || !k || !x || !out) return ENGRAM_ERR_INVALID_ARG;
+    if (((uintptr_t)table & 7u) != 0 || !aligned16(w) || !aligned16(q) || !aligned16(k) ||
+        !aligned16(x) || !aligned16(out))
+        return ENGRAM_ERR_INVALID_ARG;
+    return ENGRAM_OK;
+}
+
+// The forward's launches on a checked call, with its workspace (at least
+// engram_forward_workspace_size bytes, 256-byte aligned; nothing in it needs
+// to hold anything on entry).
+engram_status forward_launch(const engram_geometry* g, const engram_hash_tables* t,
+                             const uint8_t* table, const uint8_t* scales, const uint16_t* w,
+                             const uint16_t* q, const uint16_t* k, int32_t* state,
+                             const uint16_t* x, const int32_t* ids, const uint8_t* mask,
+                             int32_t B, int32_t T, uint16_t* out, float* gate, void* workspace,
+                             uint32_t* err, void* stream) {
+    const int64_t n_tok = (int64_t)B * T;
+    const Geom gg = engram::make_geom(*g);
+    const FwdWorkspace f = carve(gg, n_tok, workspace);
+    int32_t* hash_ids = f.hash_ids;
+    uint16_t* rows = f.rows;  // or the fused projection's scratch
+    uint16_t* kv = f.kv;
+    int32_t* live_idx = f.live_idx;
+    int32_t* rowmap = f.rowmap;
+    int* m_live = f.m_live;
+    hipStream_t s = (hipStream_t)stream;
+    // the fused gather + projection where its layout applies: 256-wide tiles
+    // for prefill-sized batches, 64-wide ones for decode-sized batches;
+    // gather then projection in between and otherwise
+    const bool fused = (n_tok >= 1024 || n_tok <= 256) && aligned16(table) &&
+                       engram::gathered_supported(gg, n_tok);
+    if (fused && engram::gate_partials_supported(gg, n_tok)) {
+        // fully fused: the hash writes the projection's row offsets and
+        // scales directly; the projection reduces the key columns into the
+        // gate's partial sums and stores only the value; kv's region holds both
+        // With a mask, only live positions are projected: they are packed
+        // in order into the first rows (v and part then hold compact rows).
+        uint16_t* v = kv;
+        float2* part = reinterpret_cast<float2*>(
+            reinterpret_cast<char*>(kv) + align256((size_t)n_tok * gg.dim * sizeof(uint16_t)));
+        engram::GatePartials gp{x, q, k, part, gg.dim, gg.hc};
+        if (mask) {
+            gp.m_live = m_live;
+            gp.rowmap = rowmap;
+        }
+        hipError_t e = engram::launch_hash_prep(gg, *t, state, ids, B, T, scales, q, k, rows, err,
+                                                s, mask, live_idx, rowmap, m_live);
+        if (e == hipSuccess)
+            e = engram::launch_wkv_gate_partials(gg, nullptr, table, scales, w, n_tok, gp, v, rows,
+                                                 err, s, /*prepared=*/true);
+        if (e == hipSuccess)
+            e = engram::launch_gate_from_partials(gg, x, v, part, mask, n_tok, out, gate, s,
+                                                  mask ? live_idx : nullptr);
+        return from_hip(e);
+    }
+    hipError_t e;
+    if (fused) {
+        e = engram::launch_hash_prep(gg, *t, state, ids, B, T, scales, nullptr, nullptr, rows, err,
+                                     s);
+        if (e == hipSuccess)
+            e = engram::launch_wkv_gathered(gg, nullptr, table, scales, w, n_tok, kv, rows, err, s,
+                                            /*prepared=*/true);
+    } else {
+        e = engram::launch_hash(gg, *t, state, ids, B, T, hash_ids, err, s);
+        if (e == hipSuccess)
+            e = engram::launch_gather(gg, table, scales, hash_ids, n_tok, rows, err, s);
+        if (e == hipSuccess) e = engram::launch_wkv(rows, w, n_tok, gg.N, gg.K, kv, s);
+    }
+    if (e == hipSuccess) e = engram::launch_gate_add(gg, x, kv, q, k, mask, n_tok, out, gate, s);
+    return from_hip(e);
+}
+
+}  // namespace engram
+
 extern "C" {
 
 const char* engram_status_string(engram_status s) {
@@ -80,6 +168,7 @@ const char* engram_status_string(engram_status s) {
         case ENGRAM_ERR_UNSUPPORTED: return "unsupported geometry";
         case ENGRAM_ERR_WORKSPACE: return "workspace missing or too small";
         case ENGRAM_ERR_HIP: return "HIP runtime error";
+        case ENGRAM_ERR_TOO_LARGE: return "call needs more than the fixed scratch array holds";
     }
     return "unknown status";
 }
@@ -284,73 +373,14 @@ engram_status engram_forward(const engram_geometry* g, const engram_hash_tables*
                              const uint16_t* x, const int32_t* ids, const uint8_t* mask,
                              int32_t B, int32_t T, uint16_t* out, float* gate, void* workspace,
                              size_t workspace_bytes, uint32_t* err, void* stream) {
-    engram_status st = engram_check_geometry(g);
-    if (st != ENGRAM_OK) return st;
-    if (t == nullptr || B < 0 || T < 0) return ENGRAM_ERR_INVALID_ARG;
-    const int64_t n_tok = (int64_t)B * T;
-    if (n_tok >= kMaxTokens) return ENGRAM_ERR_INVALID_ARG;
-    if (n_tok == 0) return ENGRAM_OK;
-    if (!t->token_map || !t->mult || !t->prime || !t->offset || !ids) return ENGRAM_ERR_INVALID_ARG;
-    if (!table || !scales || !w || !q || !k || !x || !out) return ENGRAM_ERR_INVALID_ARG;
-    if (((uintptr_t)table & 7u) != 0 || !aligned16(w) || !aligned16(q) || !aligned16(k) ||
-        !aligned16(x) || !aligned16(out))
-        return ENGRAM_ERR_INVALID_ARG;
-    const size_t need = engram_forward_workspace_size(g, n_tok);
+    const engram_status st =
+        engram::forward_check(g, t, table, scales, w, q, k, x, ids, B, T, out);
+    if (st != ENGRAM_OK || (int64_t)B * T == 0) return st;
+    const size_t need = engram_forward_workspace_size(g, (int64_t)B * T);
     if (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
         return ENGRAM_ERR_WORKSPACE;
-    const Geom gg = engram::make_geom(*g);
-    const FwdWorkspace f = carve(gg, n_tok, workspace);
-    int32_t* hash_ids = f.hash_ids;
-    uint16_t* rows = f.rows;  // or the fused projection's scratch
-    uint16_t* kv = f.kv;
-    int32_t* live_idx = f.live_idx;
-    int32_t* rowmap = f.rowmap;
-    int* m_live = f.m_live;
-    hipStream_t s = (hipStream_t)stream;
-    // the fused gather + projection where its layout applies: 256-wide tiles
-    // for prefill-sized batches, 64-wide ones for decode-sized batches;
-    // gather then projection in between and otherwise
-    const bool fused = (n_tok >= 1024 || n_tok <= 256) && aligned16(table) &&
-                       engram::gathered_supported(gg, n_tok);
-    if (fused && engram::gate_partials_supported(gg, n_tok)) {
-        // fully fused: the hash writes the projection's row offsets and
-        // scales directly; the projection reduces the key columns into the
-        // gate's partial sums and stores only the value; kv's region holds both
-        // With a mask, only live positions are projected: they are packed
-        // in order into the first rows (v and part then hold compact rows).
-        uint16_t* v = kv;
-        float2* part = reinterpret_cast<float2*>(
-            reinterpret_cast<char*>(kv) + align256((size_t)n_tok * gg.dim * sizeof(uint16_t)));
-        engram::GatePartials gp{x, q, k, part, gg.dim, gg.hc};
-        if (mask) {
-            gp.m_live = m_live;
-            gp.rowmap = rowmap;
-        }
-        hipError_t e = engram::launch_hash_prep(gg, *t, state, ids, B, T, scales, q, k, rows, err,
-                                                s, mask, live_idx, rowmap, m_live);
-        if (e == hipSuccess)
-            e = engram::launch_wkv_gate_partials(gg, nullptr, table, scales, w, n_tok, gp, v, rows,
-                                                 err, s, /*prepared=*/true);
-        if (e == hipSuccess)
-            e = engram::launch_gate_from_partials(gg, x, v, part, mask, n_tok, out, gate, s,
-                                                  mask ? live_idx : nullptr);
-        return from_hip(e);
-    }
-    hipError_t e;
-    if (fused) {
-        e = engram::launch_hash_prep(gg, *t, state, ids, B, T, scales, nullptr, nullptr, rows, err,
-                                     s);
-        if (e == hipSuccess)
-            e = engram::launch_wkv_gathered(gg, nullptr, table, scales, w, n_tok, kv, rows, err, s,
-                                            /*prepared=*/true);
-    } else {
-        e = engram::launch_hash(gg, *t, state, ids, B, T, hash_ids, err, s);
-        if (e == hipSuccess)
-            e = engram::launch_gather(gg, table, scales, hash_ids, n_tok, rows, err, s);
-        if (e == hipSuccess) e = engram::launch_wkv(rows, w, n_tok, gg.N, gg.K, kv, s);
-    }
-    if (e == hipSuccess) e = engram::launch_gate_add(gg, x, kv, q, k, mask, n_tok, out, gate, s);
-    return from_hip(e);
+    return engram::forward_launch(g, t, table, scales, w, q, k, state, x, ids, mask, B, T, out,
+                                  gate, workspace, err, stream);
 }
 
 engram_status engram_forward_hashed(const engram_geometry* g, const uint8_t* table,

@@ -166,4 +166,17 @@ hipError_t launch_gate_add(const Geom& g, const uint16_t* x, const uint16_t* kv,
                            const uint16_t* q, const uint16_t* k, const uint8_t* mask,
                            int64_t n_tok, uint16_t* out, float* gate, hipStream_t s);
 
+// engram_forward split at its workspace: every other argument check, and the
+// launches given a workspace of engram_forward_workspace_size bytes.
+engram_status forward_check(const engram_geometry* g, const engram_hash_tables* t,
+                            const uint8_t* table, const uint8_t* scales, const uint16_t* w,
+                            const uint16_t* q, const uint16_t* k, const uint16_t* x,
+                            const int32_t* ids, int32_t B, int32_t T, const uint16_t* out);
+engram_status forward_launch(const engram_geometry* g, const engram_hash_tables* t,
+                             const uint8_t* table, const uint8_t* scales, const uint16_t* w,
+                             const uint16_t* q, const uint16_t* k, int32_t* state,
+                             const uint16_t* x, const int32_t* ids, const uint8_t* mask,
+                             int32_t B, int32_t T, uint16_t* out, float* gate, void* workspace,
+                             uint32_t* err, void* stream);
+
 }  // namespace engram

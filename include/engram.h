@@ -37,7 +37,8 @@ typedef enum engram_status {
     ENGRAM_ERR_INVALID_ARG = 1,   /* null pointer, negative size, bad shape */
     ENGRAM_ERR_UNSUPPORTED = 2,   /* geometry outside what the kernels handle */
     ENGRAM_ERR_WORKSPACE = 3,     /* workspace missing or too small */
-    ENGRAM_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+    ENGRAM_ERR_HIP = 4,           /* a HIP runtime call or kernel launch failed */
+    ENGRAM_ERR_TOO_LARGE = 5      /* the call needs more than the fixed scratch array */
 } engram_status;
 
 /* Bits OR-ed into the optional device error word. */
@@ -250,6 +251,29 @@ engram_status engram_forward_hashed(const engram_geometry* g, const uint8_t* tab
                                     const int32_t* hash_ids, const uint8_t* mask, int64_t n_tok,
                                     uint16_t* out, float* gate, void* workspace,
                                     size_t workspace_bytes, uint32_t* err, void* stream);
+
+/* For callers that cannot allocate device memory, or pass none (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * engram_forward with its workspace taken from a fixed array the library
+ * holds in device memory (ENGRAM_FIXED_SCRATCH_BYTES, 32 MiB, one copy per
+ * GPU the library runs on, kept until the process ends).  The call allocates
+ * nothing and frees nothing.  Arguments, outputs and errors are as in
+ * engram_forward; every output equals engram_forward's for the same inputs.
+ * A call whose engram_forward_workspace_size(g, B*T) exceeds the array
+ * returns ENGRAM_ERR_TOO_LARGE and launches nothing (at dim 5120, hc 4 and 24
+ * hash columns that is more than 600 positions: decode-sized batches fit).
+ * The device that is current must be the stream's device.  Every call on a
+ * GPU uses that GPU's one array, which keeps the last call's contents (the
+ * forward needs none of them): calls that overlap on one GPU (other threads,
+ * other streams) race and must be serialised by the caller. */
+#define ENGRAM_FIXED_SCRATCH_BYTES (32u * 1024u * 1024u)
+size_t engram_fixed_scratch_bytes(void);
+engram_status engram_forward_noalloc(const engram_geometry* g, const engram_hash_tables* t,
+                                     const uint8_t* table, const uint8_t* scales,
+                                     const uint16_t* w, const uint16_t* q, const uint16_t* k,
+                                     int32_t* state, const uint16_t* x, const int32_t* ids,
+                                     const uint8_t* mask, int32_t B, int32_t T, uint16_t* out,
+                                     float* gate, uint32_t* err, void* stream);
 
 #ifdef __cplusplus
 }

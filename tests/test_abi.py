@@ -183,3 +183,29 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         ge.engram_wkv(g, torch.zeros(4, 1536, dtype=torch.bfloat16),
                       torch.zeros(25600, 1536, dtype=torch.bfloat16))
+
+
+def test_forward_noalloc_host_checks():
+    # the fixed-scratch forward: every engram_forward argument check, then a
+    # size check against the fixed array, all before anything touches a GPU
+    lib = ge.load()
+    assert lib.engram_fixed_scratch_bytes() == 32 << 20
+    assert lib.engram_status_string(5) == b"call needs more than the fixed scratch array holds"
+    g = good()
+    fake = C.c_void_p(1 << 20)           # never dereferenced: every call below fails validation
+    ht = ge.HashTables(fake, fake, fake, fake)
+
+    def call(B, T, ids=fake, x=fake, out=fake):
+        return lib.engram_forward_noalloc(C.byref(g), C.byref(ht), fake, fake, fake, fake, fake,
+                                          None, x, ids, None, B, T, out, None, None, None)
+    assert call(1, 8, ids=None) == 1
+    assert call(1, 8, out=None) == 1
+    assert call(-1, 8) == 1
+    assert call(1, 8, x=C.c_void_p((1 << 20) + 2)) == 1
+    assert call(0, 8) == 0  # empty: a no-op success
+    big = 1
+    while ge.engram_forward_workspace_size(g, big) <= (32 << 20):
+        big *= 2
+    assert call(1, big) == 5
+    g.head_dim = 40
+    assert call(1, 8) == 2
