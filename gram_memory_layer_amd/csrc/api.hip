@@ -111,11 +111,10 @@ engram_status forward_launch(const engram_geometry* g, const engram_hash_tables*
     int32_t* rowmap = f.rowmap;
     int* m_live = f.m_live;
     hipStream_t s = (hipStream_t)stream;
-    // the fused gather + projection where its layout applies: 256-wide tiles
-    // for prefill-sized batches, 64-wide ones for decode-sized batches;
-    // gather then projection in between and otherwise
-    const bool fused = (n_tok >= 1024 || n_tok <= 256) && aligned16(table) &&
-                       engram::gathered_supported(gg, n_tok);
+    // the fused gather + projection wherever its layout applies (64-wide
+    // tiles up to 256 positions, 256-wide ones above); gather then the bf16
+    // projection otherwise
+    const bool fused = aligned16(table) && engram::gathered_supported(gg, n_tok);
     if (fused && engram::gate_partials_supported(gg, n_tok)) {
         // fully fused: the hash writes the projection's row offsets and
         // scales directly; the projection reduces the key columns into the
@@ -410,8 +409,7 @@ engram_status engram_forward_hashed(const engram_geometry* g, const uint8_t* tab
     int32_t* rowmap = f.rowmap;
     int* m_live = f.m_live;
     hipStream_t s = (hipStream_t)stream;
-    const bool fused = (n_tok >= 1024 || n_tok <= 256) && aligned16(table) &&
-                       engram::gathered_supported(gg, n_tok);
+    const bool fused = aligned16(table) && engram::gathered_supported(gg, n_tok);
     hipError_t e = hipSuccess;
     if (fused && engram::gate_partials_supported(gg, n_tok)) {
         uint16_t* v = kv;

@@ -246,9 +246,10 @@ def test_gate_from_partials_against_oracle(ge, dev, gp_case):
 # as the stage calls it stands for, also with bad token ids (flagged, read as
 # the pad id) and a hash column whose slots all fall past the table (flagged,
 # its rows read as zeros).  Cases: the 64-wide fused tiles (n_tok <= 256), the
-# gather + projection in between, the 256-wide fused tiles, and the fully
-# fused path with the gate's sums in the projection.
+# 256-wide fused tiles (300, 700 and 1100 positions), and the fully fused path
+# with the gate's sums in the projection.
 FWD_CASES = [((256, 3, 3, 2), 1, 37), ((256, 3, 3, 2), 3, 100), ((256, 3, 3, 2), 1, 1100),
+             ((256, 3, 3, 2), 2, 350),
              ((2048, 4, 3, 3), 1, 4096), ((256, 3, 3, 2), 5, 1), ((256, 3, 5, 2), 3, 2)]
 
 
@@ -288,10 +289,7 @@ def test_forward_equals_stage_calls(ge, dev, shape, B, T):
                                               err=err_b)
         out_b = ge.engram_gate_from_partials(g, xf, v, part, mask=mask.reshape(-1), gate=gate_b)
     else:
-        if n <= 256 or n >= 1024:
-            kv = ge.engram_wkv_gathered(g, wl.table, wl.scales, hid, wl.w, err=err_b)
-        else:
-            kv = ge.engram_wkv(g, ge.engram_gather(g, wl.table, wl.scales, hid, err=err_b), wl.w)
+        kv = ge.engram_wkv_gathered(g, wl.table, wl.scales, hid, wl.w, err=err_b)
         out_b = ge.engram_gate_add(g, xf, kv, wl.q, wl.k, mask=mask.reshape(-1), gate=gate_b)
     torch.cuda.synchronize()
     bits_err = int(err_a.item())
@@ -389,8 +387,8 @@ def test_forward_masked_compaction(ge, dev, kind, T, layout):
 # ------------------------------------------------------------------ forward from hash ids
 # The block's own signature (x, hash_ids, token_mask): the same outputs, bit
 # for bit, as the forward from token ids, on every path (64-wide fused tiles,
-# gather + projection, 256-wide fused tiles, fully fused with and without a
-# mask); and two layers hashed in one launch, then each layer's forward from
+# 256-wide fused tiles for mid-sized and larger batches, fully fused with and
+# without a mask); and two layers hashed in one launch, then each layer's forward from
 # its block of ids, equal to each layer's forward from token ids.
 @pytest.mark.parametrize("shape,T,masked", [((256, 3, 3, 2), 37, True), ((256, 3, 3, 2), 300, True),
                                             ((256, 3, 3, 2), 1100, False),
