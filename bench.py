@@ -123,7 +123,10 @@ def summarize_counters(pmc_dir, name, rocprof_args):
         lines.append("%s  (%d dispatches, median %.1f us)" % (k, len(durs), med / 1e3))
         for c in sorted(d):
             lines.append("    %-28s %14.4g" % (c, sum(d[c]) / len(d[c])))
-        if "GRBM_GUI_ACTIVE" in d:
+        # GRBM_GUI_ACTIVE carries a fixed cost of roughly 17k cycles per XCD
+        # per dispatch: a clock derived from it means something only for
+        # kernels that run much longer than that (50 us and up)
+        if "GRBM_GUI_ACTIVE" in d and med >= 50e3:
             gui = sum(d["GRBM_GUI_ACTIVE"]) / len(d["GRBM_GUI_ACTIVE"]) / N_XCD_COUNT
             lines.append("    clock (GUI_ACTIVE per XCD / median time)   %.2f GHz" % (gui / med))
             if "SQ_VALU_MFMA_BUSY_CYCLES" in d:
@@ -574,15 +577,16 @@ def decode(args):
                    state=state0)
     step_ids = synth.token_ids(cfg, B, S, name="step_ids")
     ids = [torch.from_numpy(step_ids[:, s:s + 1].copy()).to(dev) for s in range(S)]
+    # fresh activations for every step (2.6 MB each, 128 steps)
     xs = [synth.activations(cfg, B, dev, name="x_step%d" % s).reshape(B, 1, cfg.hc_mult, cfg.dim)
-          for s in range(8)]
+          for s in range(S)]
     out = torch.empty_like(xs[0])
     ws = torch.empty(ge.engram_forward_workspace_size(g, B), dtype=torch.uint8, device=dev)
     state = state0.clone()
 
     def steps():
         for s in range(S):
-            ge.engram_forward(g, tables, table, scales, w, q, k, xs[s % 8], ids[s], state=state,
+            ge.engram_forward(g, tables, table, scales, w, q, k, xs[s], ids[s], state=state,
                               out=out, workspace=ws)
 
     side = torch.cuda.Stream()
@@ -901,7 +905,20 @@ def cpu_baseline(cfg, t, table, scales, w, q, k, x, ids_np, mask, n_sample):
     el = time.perf_counter() - t0
     return {"value": round(S / el, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle", "sample": "first %d positions of the T=4096 prefill (all four "
-                                        "stages, fp64), %.1f s" % (S, el)}
+                                        "stages, fp64), %.1f s" % (S, el),
+            "nproc": len(os.sched_getaffinity(0)), "host_cpus": os.cpu_count(),
+            "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (what lscpu reports), from /proc/cpuinfo."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 if __name__ == "__main__":

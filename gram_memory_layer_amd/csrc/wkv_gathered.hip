@@ -252,22 +252,34 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
         for (int i = 0; i < NA; ++i)
             id_a[i] = __builtin_amdgcn_raw_buffer_load_b32(ro, ao_v[i], kt * col_o + m0x * 4, 0);
     };
-    auto issue_dma = [&](int kt, auto sd, const uint32_t* ia, int m0x, int n0x) {
+    // part 0: the fp8 rows and the scales; parts 1 and 2: the two halves of
+    // the W rows (spread over the k-tile's first three k-steps)
+    auto issue_dma = [&](int kt, auto sd, const uint32_t* ia, int m0x, int n0x, auto partc) {
         constexpr int SD = decltype(sd)::value;
-        const __amdgpu_buffer_rsrc_t rw = w_rsrc(n0x);
+        constexpr int PART = decltype(partc)::value;
+        if constexpr (PART == 0) {
 #pragma unroll
-        for (int i = 0; i < NA; ++i)
+            for (int i = 0; i < NA; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rt, (lds_void*)(smem + ((NW * i + wave) * G_NS + SD) * 1024), 16,
+                    ia[i] + ach[i], 0, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rt, (lds_void*)(smem + ((NW * i + wave) * G_NS + SD) * 1024), 16, ia[i] + ach[i], 0,
-                0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (lds_void*)(smem + OFF_SC + (wave * G_NS + SD) * 256), 4, sc_v,
-            kt * col_s + m0x * 8, 0, 0);
+                rs, (lds_void*)(smem + OFF_SC + (wave * G_NS + SD) * 256), 4, sc_v,
+                kt * col_s + m0x * 8, 0, 0);
+        } else {
+            const __amdgpu_buffer_rsrc_t rw = w_rsrc(n0x);
+            constexpr int I0 = PART == 1 ? 0 : NB / 2, I1 = PART == 1 ? NB / 2 : NB;
 #pragma unroll
-        for (int i = 0; i < NB; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rw, (lds_void*)(smem + OFF_W + ((NW * i + wave) * G_NS + SD) * 1024), 16, wvoff[i],
-                kt * 128, 0, 0);
+            for (int i = I0; i < I1; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rw, (lds_void*)(smem + OFF_W + ((NW * i + wave) * G_NS + SD) * 1024), 16,
+                    wvoff[i], kt * 128, 0, 0);
+        }
+    };
+    auto issue_dma_all = [&](int kt, auto sd, const uint32_t* ia, int m0x, int n0x) {
+        issue_dma(kt, sd, ia, m0x, n0x, IC<0>{});
+        issue_dma(kt, sd, ia, m0x, n0x, IC<1>{});
+        issue_dma(kt, sd, ia, m0x, n0x, IC<2>{});
     };
 
     // Fragment reads.  Row wm*WM + 32i + lrow of A lies in block
@@ -345,10 +357,13 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
     // from the fp8 read (k-steps 0 and 2 read nothing new for A, 1 and 3 read
     // the next pair's after converting), reads the next k-step's W fragments
     // and issues TI*TJ MFMAs (a fenced scheduling region).  At k-step 0 the
-    // row offsets of k-tile kt+3 are loaded and the DMA of k-tile kt+2 (whose
-    // offsets arrived one k-tile ago) is issued, offsets first so that
-    // waiting for them never waits for the newer DMA.  The last k-step is
-    // split around the hand-over barrier.
+    // row offsets of k-tile kt+3 are loaded and the DMA of k-tile kt+2's fp8
+    // rows and scales (whose offsets arrived one k-tile ago) is issued,
+    // offsets first so that waiting for them never waits for the newer DMA;
+    // k-steps 1 and 2 issue one half of its W rows each (every load of the
+    // k-tile is still issued before its hand-over, and the two waves of a
+    // SIMD do not both burst all their loads into one k-step).  The last
+    // k-step is split around the hand-over barrier.
     //   WAITN: loads issued after k-tile kt+1's DMA that may stay in flight;
     //          -1 for the last k-tile (no hand-over).
     auto k_tile = [&](int kt, auto st, auto ldids, auto dma, auto waitn) {
@@ -368,7 +383,12 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
                 const bool nx3 = P && kt + 3 >= nk, nx2 = P && kt + 2 >= nk;
                 if constexpr (LOAD_IDS) load_offs(nx3 ? kt + 3 - nk : kt + 3, nx3 ? m0n : m0c);
                 issue_dma(nx2 ? kt + 2 - nk : kt + 2, IC<(S + 2) % G_NS>{}, ia, nx2 ? m0n : m0c,
-                          nx2 ? n0n : n0c);
+                          nx2 ? n0n : n0c, IC<0>{});
+            }
+            if constexpr ((ks == 1 || ks == 2) && DMA) {
+                const bool nx2 = P && kt + 2 >= nk;
+                issue_dma(nx2 ? kt + 2 - nk : kt + 2, IC<(S + 2) % G_NS>{}, nullptr,
+                          nx2 ? m0n : m0c, nx2 ? n0n : n0c, IC<ks>{});
             }
             read_w(IC<S>{}, IC<ks + 1>{}, cur ^ 1);
             if constexpr (ks == 1) read_a(IC<S>{}, IC<1>{});
@@ -380,8 +400,10 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
             for (int r = 0; r < TI * TJ; ++r) {
                 if (r < TI) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (ks == 0 && DMA && r < 4) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
-                if (ks == 0 && DMA && r == 4) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                if (ks == 0 && DMA && r < 2) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+                if (ks == 0 && DMA && r == 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                if ((ks == 1 || ks == 2) && DMA && r < NB / 2)
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
                 if (ks == 1 && r < 5) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
                 if (ks != 1 && r < TJ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
@@ -417,12 +439,12 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
 #pragma unroll
         for (int i = 0; i < NA; ++i) ia[i] = id_a[i];
         if (nk > 1) load_offs(1, m0c);
-        issue_dma(0, IC<0>{}, ia, m0c, n0c);
+        issue_dma_all(0, IC<0>{}, ia, m0c, n0c);
         if (nk > 1) {
 #pragma unroll
             for (int i = 0; i < NA; ++i) ia[i] = id_a[i];
             if (nk > 2) load_offs(2, m0c);
-            issue_dma(1, IC<1>{}, ia, m0c, n0c);
+            issue_dma_all(1, IC<1>{}, ia, m0c, n0c);
         }
         if (nk > 2) handover<NIDS + NLOAD>();
         else if (nk > 1) handover<NLOAD>();
