@@ -192,7 +192,9 @@ __global__ void __launch_bounds__(1024) gate_kernel(
         const float fd = (float)dim;
         const float rstd = (1.0f / sqrtf(shh / fd + eps)) * (1.0f / sqrtf(skk / fd + eps));
         const float a = shwk * rstd * inv_sqrt_dim;
-        const float mag = fmaxf(fabsf(a), 1e-6f);
+        // the clamp keeps a NaN (fmaxf would drop it): a NaN a gives a NaN
+        // g, as the block's elementwise clamp on a tensor does
+        const float mag = fabsf(a) < 1e-6f ? 1e-6f : fabsf(a);
         const float sg = copysignf(sqrtf(mag), a);
         const float g = 1.0f / (1.0f + expf(-sg));
         gsh[tid] = g;

@@ -281,7 +281,9 @@ void eo_linear(int64_t M, int64_t N, int64_t K, const uint16_t* a, const uint16_
  *   rstd  = 1/sqrt(mean(h^2) + eps) * 1/sqrt(mean(key^2) + eps)
  *           -- per (token, stream), not across streams
  *   a     = sum(h * w * key) * rstd * dim^-0.5
- *   g     = sigmoid( copysign( sqrt(max(|a|, clamp)), a ) ),  clamp = fp32(1e-6)
+ *   g     = sigmoid( copysign( sqrt(max(|a|, clamp)), a ) ),  clamp = fp32(1e-6),
+ *           where the max keeps a NaN (as the block's elementwise clamp on a
+ *           tensor does): a NaN a gives a NaN g and a NaN out
  *   g     = 0 where token_mask is False
  *   out   = bf16(h + g * value)
  * All in fp64.  A masked position returns x unchanged (the block's forward
@@ -313,7 +315,7 @@ void eo_gate_and_add(int64_t n_tok, int hc, int dim, float eps, const uint16_t* 
             }
             double rstd = (1.0 / sqrt(shh / dim + e)) * (1.0 / sqrt(skk / dim + e));
             double a = dot * rstd / sqrt((double)dim);
-            double mag = fabs(a) > clamp ? fabs(a) : clamp;
+            double mag = fabs(a) < clamp ? clamp : fabs(a);  /* NaN stays NaN */
             double sg = copysign(sqrt(mag), a);
             double g = 1.0 / (1.0 + exp(-sg));
             if (!live) g = 0.0;

@@ -438,6 +438,54 @@ def test_gate_other_geometries(ge, dev, hc, dim, n_tok):
     _gate_check(ge, g, x, kv, q, k, mask=mask)
 
 
+# NaN and infinity in the inputs, in the form with one workgroup per token
+# (1100 tokens) and one per (token, stream) (6 tokens): out must carry the
+# oracle's bits wherever either is not finite (a NaN always as the canonical
+# 0x7FC0, reading R9, whatever the input NaN's sign and payload), gates must
+# be NaN exactly where the oracle's are, and every finite value must meet the
+# usual tolerances.
+@pytest.mark.parametrize("n_tok", [6, 1100])
+def test_gate_special_values(ge, dev, n_tok):
+    hc, dim = 4, 256
+    g = ge.Geometry.make(dim=dim, hc_mult=hc, max_ngram_size=2, n_heads=1, head_dim=32,
+                         num_embeddings=1, vocab=1)
+    say("gate special values, tokens", n_tok)
+    gen = torch.Generator(device=dev).manual_seed(31 + n_tok)
+    x = torch.randn((n_tok, hc, dim), generator=gen, device=dev).to(torch.bfloat16)
+    key = x.float() * (torch.rand((n_tok, hc, 1), generator=gen, device=dev) * 2 - 1)
+    key = key + 0.3 * torch.randn((n_tok, hc, dim), generator=gen, device=dev)
+    v = torch.randn((n_tok, dim), generator=gen, device=dev)
+    kv = torch.cat([key.reshape(n_tok, hc * dim), v], dim=1).to(torch.bfloat16)
+    q = (1 + 0.1 * torch.rand((hc, dim), generator=gen, device=dev)).to(torch.bfloat16)
+    k = (1 + 0.1 * torch.rand((hc, dim), generator=gen, device=dev)).to(torch.bfloat16)
+    xi, kvi = x.view(torch.int16), kv.view(torch.int16)
+    vo = hc * dim
+    xi[0, 1, 7] = 0x7FA5                      # a signalling NaN in h: stream 1 of token 0
+    kvi[1, vo + 9] = 0x7F80                   # +inf in the value
+    kvi[1, vo + 10] = 0xFF80 - 0x10000        # -inf in the value
+    kvi[2, vo + 4] = 0xFFD3 - 0x10000         # NaN with sign and payload in the value
+    kvi[3, 2 * dim + 5] = 0x7FC0              # NaN in the key of stream 2 of token 3
+    gate = torch.empty((n_tok, hc), dtype=torch.float32, device=dev)
+    out = ge.engram_gate_add(g, x, kv, q, k, gate=gate)
+    xb, kvb = bits(x), bits(kv)
+    ref_out, ref_g, ref_a = oracle.gate_and_add(xb, kvb, bits(q), bits(k), g.norm_eps)
+    ob, gg = bits(out), gate.cpu().numpy()
+    special = lambda b: (b & 0x7F80) == 0x7F80  # NaN or infinity (bf16 bits)
+    sp = special(ref_out)
+    assert np.array_equal(special(ob), sp)
+    assert np.array_equal(ob[sp], ref_out[sp])
+    assert np.all(ob[np.isnan(tolerances.bf16_value(ob))] == 0x7FC0)
+    assert np.array_equal(np.isnan(gg), np.isnan(ref_g))
+    assert np.isnan(ref_g[0, 1]) and np.isnan(ref_g[3, 2]) and sp[1, :, 9].all() and sp[2, :, 4].all()
+    # the finite rest, with the non-finite places zeroed on both sides
+    gz, rgz = np.where(np.isnan(gg), 0.0, gg), np.where(np.isnan(ref_g), 0.0, ref_g)
+    raz = np.where(np.isnan(ref_a), 0.0, ref_a)
+    tolerances.check_gate(gz, rgz, raz)
+    vb = kvb[:, vo:].copy()
+    vb[special(vb)] = 0
+    tolerances.check_out(np.where(sp, 0, ob), np.where(sp, 0, ref_out), xb, vb, gz, rgz)
+
+
 def test_gate_mask_and_in_place(ge, dev, tiny):
     say("gate mask in place")
     x, kv, q, k, _ = _gate_inputs(tiny.cfg, 40, dev, name="m")

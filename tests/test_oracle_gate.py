@@ -232,6 +232,50 @@ def test_agrees_with_fp32_torch_evaluation_of_the_gate_equations():
     assert np.array_equal(out[~live.numpy()], b(x)[~live.numpy()])
 
 
+def test_non_finite_inputs_follow_the_blocks_clamp():
+    # The block's forward clamps |a| with an elementwise clamp on a tensor,
+    # which keeps a NaN ("DeepSeek V4.1" Engram block, forward): a NaN in a
+    # stream or in its key makes that stream's a, g and every out element
+    # NaN; a NaN in the value spoils that feature only; an infinite value
+    # gives an infinite out (g > 0).  The oracle must show exactly the pattern
+    # an fp32 torch evaluation of the block's expression shows, with every
+    # NaN output as the canonical 0x7FC0 (reading R9).
+    T, hc, D = 6, 4, 64
+    g = torch.Generator().manual_seed(5)
+    x = torch.randn(T, hc, D, generator=g).to(torch.bfloat16)
+    kv = torch.randn(T, D * (hc + 1), generator=g).to(torch.bfloat16)
+    q = (1 + 0.1 * torch.rand(hc, D, generator=g)).to(torch.bfloat16)
+    k = (1 + 0.1 * torch.rand(hc, D, generator=g)).to(torch.bfloat16)
+    xi, kvi = x.view(torch.int16), kv.view(torch.int16)
+    xi[0, 1, 7] = 0x7FA5                      # a signalling NaN in stream 1 of token 0
+    kvi[1, hc * D + 9] = 0x7F80               # +inf in the value of token 1
+    kvi[1, hc * D + 10] = 0xFF80 - 0x10000    # -inf
+    kvi[2, hc * D + 4] = 0xFFD3 - 0x10000     # a negative NaN with a payload in the value
+    kvi[3, 2 * D + 5] = 0x7FC0                # NaN in the key of stream 2 of token 3
+    X, value = x.float(), kv[:, hc * D:].float()
+    gate_t = torch.empty(T, hc)
+    out_t = torch.empty(T, hc, D)
+    for s_ in range(hc):
+        keys = kv[:, s_ * D:(s_ + 1) * D].float()
+        dot = (X[:, s_] * (q[s_].float() * k[s_].float()) * keys).sum(1)
+        dot = dot * torch.rsqrt((X[:, s_] ** 2).mean(1) + 1e-6) * torch.rsqrt((keys ** 2).mean(1) + 1e-6)
+        dot = dot / math.sqrt(D)
+        gate_t[:, s_] = torch.sigmoid(torch.copysign(dot.abs().clamp_min(1e-6).sqrt(), dot))
+        out_t[:, s_] = X[:, s_] + gate_t[:, s_, None] * value
+    b = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    ob_t = b(out_t.to(torch.bfloat16))
+    out, gate, _ = oracle.gate_and_add(b(x), b(kv), b(q), b(k), 1e-6)
+    assert np.array_equal(np.isnan(gate), torch.isnan(gate_t).numpy())
+    assert np.isnan(gate[0, 1]) and np.isnan(gate[3, 2]) and np.isnan(gate).sum() == 2
+    special = lambda v: (v & 0x7F80) == 0x7F80
+    nan = lambda v: special(v) & ((v & 0x007F) != 0)
+    assert np.array_equal(special(out), special(ob_t)) and np.array_equal(nan(out), nan(ob_t))
+    assert nan(out)[0, 1].all() and nan(out)[3, 2].all() and nan(out)[2, :, 4].all()
+    assert np.all(out[nan(out)] == 0x7FC0)
+    inf = special(out) & ~nan(out)
+    assert np.array_equal(out[inf], ob_t[inf]) and inf.sum() == 2 * hc
+
+
 def test_page_counts():
     gold = json.load(open(os.path.join(GOLD, "page_counts.json")))
     cfg = synth.config("prefill")

@@ -39,7 +39,8 @@ BAND = 1e-4
 
 def bf16_value(bits) -> np.ndarray:
     b = np.asarray(bits, np.uint16).astype(np.uint32) << 16
-    return b.view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):  # signalling NaNs widen to quiet ones
+        return b.view(np.float32).astype(np.float64)
 
 
 def ulp_bf16(x) -> np.ndarray:
