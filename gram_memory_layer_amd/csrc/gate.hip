@@ -11,9 +11,14 @@
 // and after a fixed-order block reduction writes out = bf16(h + g[s]*v) from
 // the registers it already holds.  HBM traffic is the algorithmic minimum:
 // x and kv read once, out written once (nontemporal); q and k are
-// L2-resident.  (Persistent workgroups holding q and k in registers, DPP
-// reductions with one barrier per token, and fewer threads with more chunks
-// each all measured slower on the T=4096 prefill shape.)
+// L2-resident.  In the full-kv form with one workgroup per token, x, the
+// keys and the value are also loaded with the nontemporal hint, so that the
+// streamed lines do not displace q and k (65,536 tokens: 5.51 -> 5.62 TB/s;
+// T=4096: 4.93 -> 5.11 TB/s); the form from partial sums and the
+// per-(token, stream) form measured slower with it and keep plain loads.
+// (Persistent workgroups holding q and k in registers, DPP reductions with
+// one barrier per token, and fewer threads with more chunks each all
+// measured slower on the T=4096 prefill shape.)
 //
 // x and out may be the same buffer: every thread writes only the chunks it
 // has itself read, after reading them (so neither pointer is __restrict__).
@@ -39,6 +44,32 @@ __device__ __forceinline__ void st_nt(uint16_t* p, uint4 v) {
     __builtin_nontemporal_store(u, reinterpret_cast<u32x4*>(p));
 }
 
+// 16-byte load, with the nontemporal hint when NT
+template <bool NT>
+__device__ __forceinline__ uint4 ld16(const uint16_t* p) {
+    if constexpr (NT) {
+        const u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        return make_uint4(u.x, u.y, u.z, u.w);
+    } else {
+        return *reinterpret_cast<const uint4*>(p);
+    }
+}
+
+// Two fp32 -> packed bf16 (lo in the low half), round to nearest even, by
+// the hardware convert (v_cvt_pk_bf16_f32, one instruction per pair): for
+// every non-NaN input, infinities and overflow included, it equals the
+// integer rounding of f32_to_bf16; a NaN is then made the canonical 0x7FC0
+// that f32_to_bf16 gives.  (Measured: 65,536 tokens 5.63 -> 5.68 TB/s, the
+// form from partial sums 59.9 -> 58.8 us.)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+    const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    uint32_t o = __builtin_bit_cast(uint32_t, v);
+    o = (lo != lo) ? ((o & 0xFFFF0000u) | 0x7FC0u) : o;
+    o = (hi != hi) ? ((o & 0x0000FFFFu) | 0x7FC00000u) : o;
+    return o;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
@@ -62,6 +93,7 @@ __global__ void __launch_bounds__(1024) gate_kernel(
 #pragma clang fp contract(off)
     constexpr int HS = SPLIT ? 1 : HC;  // streams of this workgroup
     constexpr int NS = PART ? HS : 3 * HS;
+    constexpr bool NT = !PART && !SPLIT;  // streamed loads with the nontemporal hint
     __shared__ float red[16][NS];
     __shared__ float gsh[HS];
 
@@ -122,10 +154,10 @@ __global__ void __launch_bounds__(1024) gate_kernel(
     for (int i = 0; i < NCH; ++i) {
         const int c = tid + i * nthr;
         if (c < d8) {
-            if (KEEP) vr[i < KC ? i : 0] = *reinterpret_cast<const uint4*>(kvt + voff + c * 8);
+            if (KEEP) vr[i < KC ? i : 0] = ld16<NT>(kvt + voff + c * 8);
 #pragma unroll
             for (int s = 0; s < HS; ++s) {
-                const uint4 h = *reinterpret_cast<const uint4*>(xt + (int64_t)s * dim + c * 8);
+                const uint4 h = ld16<NT>(xt + (int64_t)s * dim + c * 8);
                 if (KEEP) xr[s][i < KC ? i : 0] = h;
                 if constexpr (PART) {
                     const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
@@ -137,7 +169,7 @@ __global__ void __launch_bounds__(1024) gate_kernel(
                     }
                 } else {
                     const int64_t so = (int64_t)(s0 + s) * dim + c * 8;
-                    const uint4 key = *reinterpret_cast<const uint4*>(kvt + so);
+                    const uint4 key = ld16<NT>(kvt + so);
                     const uint4 qq = *reinterpret_cast<const uint4*>(q + so);
                     const uint4 kk = *reinterpret_cast<const uint4*>(kw + so);
                     const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
@@ -222,7 +254,7 @@ __global__ void __launch_bounds__(1024) gate_kernel(
                 for (int e = 0; e < 4; ++e) {
                     const float r0 = __fmaf_rn(g[s], lo_f(vw[e]), lo_f(hw[e]));
                     const float r1 = __fmaf_rn(g[s], hi_f(vw[e]), hi_f(hw[e]));
-                    o[e] = f32_to_bf16(r0) | (f32_to_bf16(r1) << 16);
+                    o[e] = pack2_bf16(r0, r1);
                 }
                 st_nt(ot + (int64_t)s * dim + c * 8, make_uint4(o[0], o[1], o[2], o[3]));
             }
