@@ -260,7 +260,11 @@ def test_non_finite_inputs_follow_the_blocks_clamp():
         dot = (X[:, s_] * (q[s_].float() * k[s_].float()) * keys).sum(1)
         dot = dot * torch.rsqrt((X[:, s_] ** 2).mean(1) + 1e-6) * torch.rsqrt((keys ** 2).mean(1) + 1e-6)
         dot = dot / math.sqrt(D)
-        gate_t[:, s_] = torch.sigmoid(torch.copysign(dot.abs().clamp_min(1e-6).sqrt(), dot))
+        # g of the gate page: the sigmoid of the square root of |a| held at
+        # 1e-6 from below, carrying the sign of a; torch.clamp on a tensor
+        # keeps a NaN, as the block's clamp does
+        root = torch.sqrt(torch.clamp(dot.abs(), min=1e-6))
+        gate_t[:, s_] = 1.0 / (1.0 + torch.exp(-torch.where(dot < 0, -root, root)))
         out_t[:, s_] = X[:, s_] + gate_t[:, s_, None] * value
     b = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
     ob_t = b(out_t.to(torch.bfloat16))
