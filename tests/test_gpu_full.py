@@ -224,6 +224,49 @@ def test_forward_gate_partials_geometry(ge, dev, dim, n_heads, T, inplace):
         assert np.all(gate.cpu().numpy().reshape(T, -1)[masked] == 0)
 
 
+# Non-finite activations in the fully fused forward (reading R21): a NaN or
+# an infinity in one feature of one (position, stream) of x must turn that
+# stream's gate and whole output into NaN (0x7FC0) and leave every other
+# output bit for bit as the clean forward wrote it (positions and streams are
+# independent once the kv is formed, and x does not enter the kv).
+@pytest.mark.parametrize("T,masked", [(4096, False), (1000, False), (4096, True)])
+def test_forward_nonfinite_x_stays_in_its_stream(ge, dev, T, masked):
+    import dataclasses
+    cfg = dataclasses.replace(synth.config("prefill"), dim=2048, n_heads=3, T=T,
+                              mask_frac=0.2 if masked else 0.0)
+    say("non-finite x forward", T, "masked" if masked else "")
+    wl = Workload(ge, cfg, dev)
+    hc, dim = cfg.hc_mult, cfg.dim
+    ids = torch.from_numpy(synth.token_ids(cfg, 1, T)).to(dev)
+    x = synth.activations(cfg, T, dev).reshape(1, T, hc, dim)
+    mask = torch.from_numpy(synth.token_mask(cfg, 1, T)).to(dev) if masked else None
+    layer = ge.EngramLayer(wl.g, wl.tables, wl.table, wl.scales, wl.w, wl.q, wl.k)
+    fused = T >= 4096  # (1000 positions take the full-kv gate)
+    assert bool(ge.engram_gate_partials_supported(wl.g, T)) == fused
+    gate0 = torch.empty((1, T, hc), dtype=torch.float32, device=dev)
+    out0 = layer.forward(x, ids, mask=mask, gate=gate0)
+    live = np.ones(T, bool) if mask is None else mask.cpu().numpy().reshape(-1) != 0
+    lp = np.nonzero(live)[0]
+    plant = [(int(lp[3]), 1, 17, 0x7FC0), (int(lp[len(lp) // 2]), 3, 1000, 0x7F80),
+             (int(lp[-1]), 0, dim - 1, 0xFF80 - 0x10000)]
+    xs = x.clone()
+    for t, s_, f, v in plant:
+        xs.view(torch.int16)[0, t, s_, f] = v
+    gate1 = torch.empty_like(gate0)
+    out1 = layer.forward(xs, ids, mask=mask, gate=gate1)
+    torch.cuda.synchronize()
+    o0, o1 = bits(out0).reshape(T, hc, dim), bits(out1).reshape(T, hc, dim)
+    g0, g1 = gate0.cpu().numpy().reshape(T, hc), gate1.cpu().numpy().reshape(T, hc)
+    hit = np.zeros((T, hc), bool)
+    for t, s_, f, v in plant:
+        hit[t, s_] = True
+        assert np.isnan(g1[t, s_]), (t, s_)
+        assert np.all(o1[t, s_] == 0x7FC0), (t, s_)
+    assert np.array_equal(o1[~hit], o0[~hit])
+    assert np.array_equal(g1[~hit], g0[~hit])
+    assert not np.isnan(g0).any()
+
+
 # ------------------------------------------------------------------ projection tiling
 @pytest.mark.parametrize("M", [2048, 4096])
 def test_wkv_full_width_tail_split(ge, dev, M):
