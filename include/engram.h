@@ -174,7 +174,10 @@ engram_status engram_wkv_gathered(const engram_geometry* g, const uint8_t* table
  *   out  bf16 [n_tok, hc_mult, dim] (may be the same buffer as x: then a
  *        masked position is not touched at all);
  *   gate fp32 [n_tok, hc_mult] or NULL.
- * fp32 arithmetic with fixed-order reductions (run-to-run deterministic). */
+ * fp32 arithmetic with fixed-order reductions (run-to-run deterministic).
+ * The max in g keeps a NaN (as the block's elementwise clamp does): a NaN
+ * or an infinity in a stream or its key that makes a NaN gives that stream
+ * a NaN gate and an all-NaN out; every NaN written is 0x7FC0. */
 engram_status engram_gate_add(const engram_geometry* g, const uint16_t* x, const uint16_t* kv,
                               const uint16_t* q, const uint16_t* k, const uint8_t* mask,
                               int64_t n_tok, uint16_t* out, float* gate, void* stream);
