@@ -31,6 +31,8 @@ METRIC = "Engram prefill tokens/s @dim5120 hc4 (1 GPU); % MFMA peak (wkv), % HBM
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "wkv_gate_partials_prefill_traffic.json")
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "wkv_gathered_decode_traffic.json")
+DECODE_KERNELS = ("prep_kernel", "wkv_gathered_64")  # one engram_wkv_gathered call at M = 64
 
 
 def parse():
@@ -59,6 +61,10 @@ def parse():
                         "script (--kernel-trace --stats; --pmc FETCH_SIZE; --pmc WRITE_SIZE, "
                         "the last two with --copy-calibration) into the summaries under "
                         "profiles/")
+    p.add_argument("--summarize-decode-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="no GPU work: turn FETCH_SIZE and WRITE_SIZE runs of `--workload decode "
+                        "--copy-calibration` into the decode projection's traffic summary "
+                        "under profiles/")
     p.add_argument("--summarize-counters", nargs=3, metavar=("PMC_DIR", "NAME", "ROCPROF_ARGS"),
                    help="no GPU work: turn one rocprofv3 --pmc run of the prefill bench into "
                         "profiles/NAME.txt")
@@ -157,12 +163,13 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_record(launch_flops_tokens: int):
-    """HBM bytes per engram_wkv_gate_partials call (its three kernels) from the
-    committed rocprofv3 counter summary, or None if it was taken on a
-    different kernel source or workload."""
+def traffic_record(launch_flops_tokens: int, path: str = TRAFFIC_FILE):
+    """HBM bytes per call of the roofline's kernels (engram_wkv_gate_partials,
+    or engram_wkv_gathered at decode size) from the committed rocprofv3
+    counter summary, or None if it was taken on a different kernel source or
+    workload."""
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        rec = json.load(open(path))
     except (OSError, ValueError):
         return None
     if rec.get("source_digest") != kernel_source_digest() or rec.get("tokens") != launch_flops_tokens:
@@ -361,6 +368,52 @@ def summarize(stats_dir, fetch_dir, write_dir):
           "profiles/engram_prefill_T4096_traffic.txt, %s" % os.path.relpath(TRAFFIC_FILE, ROOT))
 
 
+def summarize_decode_traffic(fetch_dir, write_dir):
+    """HBM bytes per engram_wkv_gathered call at M = 64 (prep_kernel +
+    wkv_gathered_64, the decode roofline's kernels) from one FETCH_SIZE and one
+    WRITE_SIZE run of the decode bench, scaled by its 1 GiB calibration copy."""
+    cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc %s --kernel-trace --output-format csv "
+           "-d <out> -o <name> -- python3 <repo>/bench.py --workload decode --copy-calibration")
+    fetch, copy_f = _counter_means(fetch_dir, "FETCH_SIZE")
+    write, copy_w = _counter_means(write_dir, "WRITE_SIZE")
+    fs = COPY_BYTES / (copy_f * 1024.0)
+    ws = COPY_BYTES / (copy_w * 1024.0)
+    lines = ["# HBM traffic per dispatch from rocprofv3 counters, Engram decode B=64 (one token "
+             "per sequence), dim 5120, hc 4",
+             "# commands (two runs, one counter each; repository root = <repo>):",
+             "#   " + cmd % "FETCH_SIZE", "#   " + cmd % "WRITE_SIZE",
+             "# calibration: a device copy of exactly 1 GiB reads FETCH_SIZE = %.1f KiB (scale %.4f)"
+             % (copy_f, fs),
+             "#   and WRITE_SIZE = %.1f KiB (scale %.4f)" % (copy_w, ws),
+             "# source digest of the gathered projection (bench.kernel_source_digest): %s"
+             % kernel_source_digest(),
+             "",
+             "%-34s %14s %14s %12s %12s" % ("kernel", "FETCH_KiB", "WRITE_KiB", "fetch_MB*", "write_MB*")]
+    total = {"fetch": 0.0, "write": 0.0}
+    for k in sorted(set(fetch) | set(write)):
+        f, w_ = fetch.get(k, 0.0), write.get(k, 0.0)
+        lines.append("%-34s %14.1f %14.1f %12.2f %12.2f" % (k, f, w_, f * 1024 * fs / 1e6,
+                                                            w_ * 1024 * ws / 1e6))
+        if k.split("<")[0] in DECODE_KERNELS:
+            total["fetch"] += f * 1024 * fs
+            total["write"] += w_ * 1024 * ws
+    lines.append("# * scaled by the calibration copy; MB = 1e6 bytes.")
+    lines.append("# engram_wkv_gathered at M = 64 per call: fetch %.2f MB + write %.2f MB "
+                 "(algorithmic: W 78.64 + fp8 rows and scales 0.10 + kv 3.28 = 82.02 MB)"
+                 % (total["fetch"] / 1e6, total["write"] / 1e6))
+    open(os.path.join(ROOT, "profiles", "engram_decode_B64_traffic.txt"), "w").write(
+        "\n".join(lines) + "\n")
+    rec = {"kernel": "engram_wkv_gathered at M = 64 (" + " + ".join(DECODE_KERNELS) + ")",
+           "workload": "decode B=64 dim 5120 hc 4", "tokens": 64,
+           "source_digest": kernel_source_digest(),
+           "fetch_bytes_per_launch": int(total["fetch"]),
+           "write_bytes_per_launch": int(total["write"]),
+           "fetch_scale": fs, "write_scale": ws,
+           "hbm_bytes_per_launch": int(total["fetch"] + total["write"])}
+    json.dump(rec, open(DECODE_TRAFFIC_FILE, "w"), indent=1)
+    print("wrote profiles/engram_decode_B64_traffic.txt, %s" % os.path.relpath(DECODE_TRAFFIC_FILE, ROOT))
+
+
 def main():
     args = parse()
     if args.summarize:
@@ -371,6 +424,9 @@ def main():
         return
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
+        return
+    if args.summarize_decode_traffic:
+        summarize_decode_traffic(*args.summarize_decode_traffic)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the Engram path is built and timed per GPU "
@@ -616,6 +672,14 @@ def decode(args):
     st_proj = time_launches(lambda: ge.engram_wkv_gathered(g, table, scales, hid, w, kv=kv,
                                                            scratch=scratch), 200, stream)
     proj_bytes = g.N * g.K * 2 + B * g.n_hash_cols * (64 + 2) + B * g.N * 2
+    if args.copy_calibration:  # a 1 GiB copy for the counter runs to scale by
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     rec = {
         "metric": "Engram decode tokens/s @dim5120 hc4 (1 GPU), B=64, 128 steps after 512",
         "value": round(B / sec, 1), "unit": "tokens/s", "n_gpus": 1, "steps": S * reps,
@@ -628,7 +692,7 @@ def decode(args):
         "roofline": {"kernel": "engram_wkv_gathered (M=64)", "bound": "hbm",
                      "achieved": round(proj_bytes / st_proj / 1e9, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(proj_bytes / st_proj / 1e9 / PEAK_HBM_GBS, 4),
-                     "traffic": None},
+                     "traffic": traffic_record(B, DECODE_TRAFFIC_FILE)},
         "eager_ms_per_step": round(eager * 1e3, 4),
         "projection_us": round(st_proj * 1e6, 2),
         "wall_s": round(wall, 3),
