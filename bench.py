@@ -477,14 +477,27 @@ def main():
         ge.engram_forward(g, tables, table, scales, w, q, k, x, ids, mask=mask, out=out,
                           workspace=ws)
 
-    for _ in range(args.warmup):
+    # The cold-cache forwards and then the stage timings run before the
+    # forward's warm-up and timed steps: the timed forwards then run at the
+    # clocks the part holds under load (after an idle phase a few warm-up
+    # forwards leave it in its clock ramp, 3-4% slower at 20 warm-up forwards
+    # than at 200), and after stage work that leaves no flushed lines behind.
+
+    # the same forward with the caches cold: a 512 MiB write (past the 256 MB
+    # MALL and the 8 x 4 MB L2) between forwards, each forward timed alone
+    flush = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
+    cold = []
+    for _ in range(10):
+        flush.fill_(1)
+        s0 = torch.cuda.Event(enable_timing=True)
+        s1 = torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
         step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    sec = time_launches(step, args.steps, stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    tokens_per_s = n_tok / sec
+        s1.record(stream)
+        s1.synchronize()
+        cold.append(s0.elapsed_time(s1))
+    del flush
+    cold_ms = sorted(cold)[len(cold) // 2]
 
     # ---- per-stage launch times (each stage alone, same inputs, same stream).
     # The forward runs hash_prep_kernel (the hash written straight as the
@@ -507,13 +520,7 @@ def main():
     ge.engram_wkv_gathered(g, table, scales, hid, w, kv=kv, scratch=scratch)
     ge.engram_gate_add(g, x, kv, q, k, mask=mask, out=out)
     torch.cuda.synchronize()
-    reps = max(args.steps, 10)
-    st_hash = time_launches(lambda: ge.engram_hash(g, tables, ids, hash_ids=hid), reps, stream)
-    st_proj = time_launches(
-        lambda: ge.engram_wkv_gate_partials(g, table, scales, hid, w, xf, q, k, v=v, part=part,
-                                            scratch=scratch), reps, stream)
-    st_pgate = time_launches(
-        lambda: ge.engram_gate_from_partials(g, xf, v, part, mask=mask, out=outf), reps, stream)
+    reps = max(args.steps, 50)
     st_gather = time_launches(lambda: ge.engram_gather(g, table, scales, hid, rows=rows), reps, stream)
     st_wkv = time_launches(lambda: ge.engram_wkv(g, rows, w, kv=kv), reps, stream)
     st_fused = time_launches(
@@ -521,22 +528,21 @@ def main():
         stream)
     st_gate = time_launches(lambda: ge.engram_gate_add(g, x, kv, q, k, mask=mask, out=out), reps,
                             stream)
+    st_hash = time_launches(lambda: ge.engram_hash(g, tables, ids, hash_ids=hid), reps, stream)
+    st_proj = time_launches(
+        lambda: ge.engram_wkv_gate_partials(g, table, scales, hid, w, xf, q, k, v=v, part=part,
+                                            scratch=scratch), reps, stream)
+    st_pgate = time_launches(
+        lambda: ge.engram_gate_from_partials(g, xf, v, part, mask=mask, out=outf), reps, stream)
 
-    # the same forward with the caches cold: a 512 MiB write (past the 256 MB
-    # MALL and the 8 x 4 MB L2) between forwards, each forward timed alone
-    flush = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
-    cold = []
-    for _ in range(10):
-        flush.fill_(1)
-        s0 = torch.cuda.Event(enable_timing=True)
-        s1 = torch.cuda.Event(enable_timing=True)
-        s0.record(stream)
+    for _ in range(args.warmup):
         step()
-        s1.record(stream)
-        s1.synchronize()
-        cold.append(s0.elapsed_time(s1))
-    del flush
-    cold_ms = sorted(cold)[len(cold) // 2]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    sec = time_launches(step, args.steps, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tokens_per_s = n_tok / sec
 
     flops_per_token = 2 * g.K * g.N
     wkv_flops = flops_per_token * n_tok
