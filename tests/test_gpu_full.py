@@ -309,6 +309,7 @@ def test_decode_full(ge, dev):
     assert np.array_equal(got_pre.cpu().numpy(), ref_pre)
     layer = ge.EngramLayer(wl.g, wl.tables, wl.table, wl.scales, wl.w, wl.q, wl.k)
     check_steps = {0, 1, 2, 63, S - 1}
+    masked_steps = {1, 63}  # a quarter of the sequences masked (still hashed)
     rows_to_check = np.arange(B)  # every sequence of a checked step
     for step in range(S):
         ids_s = steps[:, step:step + 1].copy()
@@ -318,7 +319,11 @@ def test_decode_full(ge, dev):
         got_h = ge.engram_hash(wl.g, wl.tables, ids_t, state=probe)
         x = synth.activations(cfg, B, dev, name="x_step%d" % step).reshape(B, 1, cfg.hc_mult, cfg.dim)
         gate = torch.empty((B, 1, cfg.hc_mult), dtype=torch.float32, device=dev)
-        out = layer.forward(x, ids_t, state=state, gate=gate)
+        mk = None
+        if step in masked_steps:
+            mk = np.random.default_rng(step).random(B) >= 0.25
+        out = layer.forward(x, ids_t, state=state, gate=gate,
+                            mask=None if mk is None else torch.from_numpy(mk).reshape(B, 1).to(dev))
         assert np.array_equal(got_h.cpu().numpy(), ref_h), step
         assert torch.equal(state, probe), step
         if step in check_steps:
@@ -328,8 +333,13 @@ def test_decode_full(ge, dev):
             rows = oracle.embed_rows(tab, sc, inv.reshape(-1)).reshape(len(rows_to_check), -1)
             kv = oracle.linear(rows, bits(wl.w))
             xb = bits(x).reshape(B, cfg.hc_mult, cfg.dim)[rows_to_check]
-            r_out, r_gate, r_a = oracle.gate_and_add(xb, kv, bits(wl.q), bits(wl.k), cfg.norm_eps)
+            r_out, r_gate, r_a = oracle.gate_and_add(xb, kv, bits(wl.q), bits(wl.k), cfg.norm_eps,
+                                                     None if mk is None else mk[rows_to_check])
             ref = dict(rows=rows, kv=kv, out=r_out, gate=r_gate, a=r_a)
+            if mk is not None:  # masked sequences: x bit for bit, gate 0
+                ob = bits(out).reshape(B, cfg.hc_mult, cfg.dim)
+                assert np.array_equal(ob[~mk], bits(x).reshape(B, cfg.hc_mult, cfg.dim)[~mk])
+                assert np.all(gate.cpu().numpy().reshape(B, -1)[~mk] == 0)
             st = _check_tokens(ref, bits(out).reshape(B, cfg.hc_mult, cfg.dim)[rows_to_check],
                                gate.cpu().numpy().reshape(B, -1)[rows_to_check], xb, wl,
                                min_tight=DECODE_FLOORS["gate_tight"],
