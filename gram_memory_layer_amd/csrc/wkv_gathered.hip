@@ -276,11 +276,6 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
                     wvoff[i], kt * 128, 0, 0);
         }
     };
-    auto issue_dma_all = [&](int kt, auto sd, const uint32_t* ia, int m0x, int n0x) {
-        issue_dma(kt, sd, ia, m0x, n0x, IC<0>{});
-        issue_dma(kt, sd, ia, m0x, n0x, IC<1>{});
-        issue_dma(kt, sd, ia, m0x, n0x, IC<2>{});
-    };
 
     // Fragment reads.  Row wm*WM + 32i + lrow of A lies in block
     // (wm*WM + lrow)/16 + 2i, W row wn*WN + 32j + lrow in block
@@ -441,22 +436,32 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
     using W0 = IC<0>;
     using Wn = IC<-1>;
 
-    // prologue: k-tiles 0 and 1 in flight, offsets of k-tile 2 loaded
+    // prologue: k-tiles 0 and 1 in flight, offsets of k-tile 2 loaded.  The
+    // W rows of both go first: they need no row offsets, so they stream
+    // while the offsets make their round trip.
     {
+        issue_dma(0, IC<0>{}, nullptr, m0c, n0c, IC<1>{});
+        issue_dma(0, IC<0>{}, nullptr, m0c, n0c, IC<2>{});
+        if (nk > 1) {
+            issue_dma(1, IC<1>{}, nullptr, m0c, n0c, IC<1>{});
+            issue_dma(1, IC<1>{}, nullptr, m0c, n0c, IC<2>{});
+        }
         load_offs(0, m0c);
         uint32_t ia[NA];
 #pragma unroll
         for (int i = 0; i < NA; ++i) ia[i] = id_a[i];
         if (nk > 1) load_offs(1, m0c);
-        issue_dma_all(0, IC<0>{}, ia, m0c, n0c);
+        issue_dma(0, IC<0>{}, ia, m0c, n0c, IC<0>{});
         if (nk > 1) {
 #pragma unroll
             for (int i = 0; i < NA; ++i) ia[i] = id_a[i];
             if (nk > 2) load_offs(2, m0c);
-            issue_dma_all(1, IC<1>{}, ia, m0c, n0c);
+            issue_dma(1, IC<1>{}, ia, m0c, n0c, IC<0>{});
         }
-        if (nk > 2) handover<NIDS + NLOAD>();
-        else if (nk > 1) handover<NLOAD>();
+        // k-tile 0 has landed once at most the loads issued after its fp8
+        // rows are in flight (the offsets of k-tile 2, k-tile 1's rows)
+        if (nk > 2) handover<NIDS + NA + 1>();
+        else if (nk > 1) handover<NA + 1>();
         else handover<0>();
         read_a(IC<0>{}, IC<0>{});
         read_w(IC<0>{}, IC<0>{}, 0);
