@@ -144,6 +144,7 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
     static_assert(NA >= 1 && NB >= 1 && TI >= 1 && TJ % 2 == 0, "tile shape");
     constexpr int OFF_SC = (BT / 16) * G_NS * 1024;
     constexpr int OFF_W = OFF_SC + NW * G_NS * 256;
+    constexpr int OFF_WQK = OFF_W + (BT / 8) * G_NS * 1024;  // q*k, 512 bytes per wave (G only)
     constexpr int NLOAD = NA + 1 + NB;  // DMA per wave per k-tile
     constexpr int NIDS = NA;            // row-offset loads per wave per k-tile
 
@@ -491,60 +492,104 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
 #pragma clang fp contract(off)
             typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
             typedef float f32x4 __attribute__((ext_vector_type(4)));
+            constexpr int NQ = TI * TJ;  // quarters: 32 rows x 32 columns each
             const int s = n0c / gp.dim, f0 = n0c - s * gp.dim + wn * WN;
             const int nq = gp.dim >> 7;
             const __amdgpu_buffer_rsrc_t rx =
                 make_rsrc(gp.x, (uint32_t)(M * gp.hc * gp.dim * 2));  // rows past M read 0
-            // this wave's 128 values of q*k, staged in its first stage-2 block
-            // (stage 2 is unused here: key tiles store nothing)
-            const uint32_t wl = blk(0);
+            // this wave's 128 values of q*k
+            const uint32_t wl = (uint32_t)(OFF_WQK + wave * 512);
             if (lane < 32)
                 *reinterpret_cast<uint4*>(smem + wl + lane * 16) =
                     *reinterpret_cast<const uint4*>(gp.wqk + s * gp.dim + f0 + lane * 4);
+            // x arrives by DMA in quarters (the 32 rows of one i, the 32
+            // columns of one j: 64 bytes per row), each in two of this wave's
+            // stage-2 blocks, three quarters in flight.  DMA lane L of block t
+            // moves 16 bytes of row 16t + L/4 of the quarter: logical chunk
+            // (L%4) ^ (row/4 % 4), stored at slot L%4 of the row's 64 bytes,
+            // so that the fragment-layout reads below spread over the banks.
+            // Each DMA instruction reads whole 64-byte row pieces of 16 rows;
+            // loading x straight into the fragment layout (8 bytes per lane,
+            // 32 rows per instruction) kept the address unit busy on 32 cache
+            // lines per instruction, four times as many per byte, and cost
+            // 17 us more per prefill forward at T=4096.  (Padding rows past M,
+            // whose sums are not stored, may wrap the 32-bit offset: the read
+            // then stays inside x.)
+            uint32_t xo[TI][2];
+#pragma unroll
+            for (int i = 0; i < TI; ++i)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int rr = 16 * t + (lane >> 2);
+                    const int64_t m = (int64_t)m0c + wm * WM + i * 32 + rr;
+                    // the position of row m (compacted: from the row map, which
+                    // points rows past the live count past x, where loads read 0)
+                    const int64_t xm = rowmap ? (int64_t)rowmap[m] : m;
+                    const int c = (lane & 3) ^ ((rr >> 2) & 3);
+                    xo[i][t] = (uint32_t)(((xm * gp.hc + s) * gp.dim + f0) * 2) + (uint32_t)(c * 16);
+                }
+            auto issue_q = [&](int q) {
+                const int i = q / TJ, j = q % TJ, b = q % 3;
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rx, (lds_void*)(smem + blk(2 * b + t)), 16, xo[i][t], j * 64, 0, 0);
+            };
+            const int sw = (lrow >> 2) & 3;
+            issue_q(0);
+            issue_q(1);
+            issue_q(2);
+            float skk = 0.0f, shwk = 0.0f;
+            float2 res[TI];
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const int i = q / TJ, j = q % TJ, b = q % 3;
+                // quarter q has landed once only the quarters issued after it
+                // (two DMA instructions each) may still be in flight
+                if (NQ - 1 - q >= 2) __builtin_amdgcn_s_waitcnt(0x0F74);       // vmcnt(4)
+                else if (NQ - 1 - q == 1) __builtin_amdgcn_s_waitcnt(0x0F72);  // vmcnt(2)
+                else __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0)
+                const uint32_t rb = blk(2 * b + (lrow >> 4)) + (lrow & 15) * 64 + lhalf * 8;
+                u32x2 h4[4];
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4)
+                    h4[g4] = *reinterpret_cast<const u32x2*>(smem + rb + ((g4 ^ sw) << 4));
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the buffer is free again
+                if (q + 3 < NQ) issue_q(q + 3);
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int nl = j * 32 + 8 * g4 + 4 * lhalf;
+                    const f32x4 ww = *reinterpret_cast<const f32x4*>(smem + wl + nl * 4);
+                    const uint32_t kb[2] = {
+                        pack_bf16(acc[j][i][4 * g4 + 0], acc[j][i][4 * g4 + 1]),
+                        pack_bf16(acc[j][i][4 * g4 + 2], acc[j][i][4 * g4 + 3])};
+                    const u32x2 h2 = h4[g4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int sh = (e & 1) ? 0 : 16;  // low half first
+                        const float key = __uint_as_float((kb[e >> 1] << sh) & 0xFFFF0000u);
+                        const float h = __uint_as_float((h2[e >> 1] << sh) & 0xFFFF0000u);
+                        // key^2 is exact in fp32, so the fused form rounds the
+                        // same sum; (h*w)*key is rounded before the add
+                        skk = __builtin_fmaf(key, key, skk);
+                        shwk += (h * ww[e]) * key;
+                    }
+                }
+                if (j == TJ - 1) {
+                    skk += __shfl_xor(skk, 32, 64);
+                    shwk += __shfl_xor(shwk, 32, 64);
+                    res[i] = make_float2(skk, shwk);
+                    skk = 0.0f;
+                    shwk = 0.0f;
+                }
+            }
 #pragma unroll
             for (int i = 0; i < TI; ++i) {
                 const int64_t m = (int64_t)m0c + wm * WM + i * 32 + lrow;
-                // the position of row m (compacted: from the row map, which
-                // points rows past the live count past x, where loads read 0)
-                const int64_t xm = rowmap ? (int64_t)rowmap[m] : m;
-                const uint32_t xr = (uint32_t)(((xm * gp.hc + s) * gp.dim + f0) * 2);
-                // all of the row's h values for this lane first (one round trip)
-                u32x2 hx[TJ * 4];
-#pragma unroll
-                for (int j = 0; j < TJ; ++j)
-#pragma unroll
-                    for (int g4 = 0; g4 < 4; ++g4)
-                        hx[j * 4 + g4] = __builtin_amdgcn_raw_buffer_load_b64(
-                            rx, xr + (uint32_t)(j * 32 + 8 * g4 + 4 * lhalf) * 2, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
-                float skk = 0.0f, shwk = 0.0f;
-#pragma unroll
-                for (int j = 0; j < TJ; ++j)
-#pragma unroll
-                    for (int g4 = 0; g4 < 4; ++g4) {
-                        const int nl = j * 32 + 8 * g4 + 4 * lhalf;
-                        const f32x4 ww = *reinterpret_cast<const f32x4*>(smem + wl + nl * 4);
-                        const uint32_t kb[2] = {
-                            pack_bf16(acc[j][i][4 * g4 + 0], acc[j][i][4 * g4 + 1]),
-                            pack_bf16(acc[j][i][4 * g4 + 2], acc[j][i][4 * g4 + 3])};
-                        const u32x2 h2 = hx[j * 4 + g4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int sh = (e & 1) ? 0 : 16;  // low half first
-                            const float key = __uint_as_float((kb[e >> 1] << sh) & 0xFFFF0000u);
-                            const float h = __uint_as_float((h2[e >> 1] << sh) & 0xFFFF0000u);
-                            // key^2 is exact in fp32, so the fused form rounds the
-                            // same sum; (h*w)*key is rounded before the add
-                            skk = __builtin_fmaf(key, key, skk);
-                            shwk += (h * ww[e]) * key;
-                        }
-                    }
-                skk += __shfl_xor(skk, 32, 64);
-                shwk += __shfl_xor(shwk, 32, 64);
-                if (lhalf == 0 && m < M)
-                    gp.part[(m * gp.hc + s) * nq + (f0 >> 7)] = make_float2(skk, shwk);
+                if (lhalf == 0 && m < M) gp.part[(m * gp.hc + s) * nq + (f0 >> 7)] = res[i];
             }
-            // the next tile's DMA may refill stage 2 only after this wave's w reads
+            // the next tile's DMA may refill stage 2 only after every wave is
+            // done with its x quarters there
             __builtin_amdgcn_s_waitcnt(0xC07F);
             asm volatile("s_barrier" ::: "memory");
         };
@@ -659,7 +704,8 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
     }
 }
 
-constexpr int SMEM256 = (256 / 16) * G_NS * 1024 + 8 * G_NS * 256 + (256 / 8) * G_NS * 1024;
+constexpr int SMEM256 = (256 / 16) * G_NS * 1024 + 8 * G_NS * 256 + (256 / 8) * G_NS * 1024 +
+                        8 * 512;  // + the gate partials' q*k
 constexpr int SMEM128 = (128 / 16) * G_NS * 1024 + 4 * G_NS * 256 + (128 / 8) * G_NS * 1024;
 static_assert(SMEM256 <= 160 * 1024, "LDS budget");
 static_assert(8 * 128 * 128 <= SMEM256 && 4 * 64 * 128 <= SMEM128, "epilogue staging fits the ring");
