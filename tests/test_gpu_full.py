@@ -187,16 +187,21 @@ MID_FLOORS = dict(gate_tight=0.89, gate_max_rel=9.4e-4, out_beyond_2ulp=1.6e-4)
 
 
 # ------------------------------------------------------------------ fully fused prefill
-@pytest.mark.parametrize("dim,n_heads,T,inplace", [(2048, 3, 4096, False), (2048, 3, 4000, True)])
-def test_forward_gate_partials_geometry(ge, dev, dim, n_heads, T, inplace):
-    # a smaller geometry that still takes the fully fused path (gate sums in
-    # the projection's epilogue): dim 2048, 6 hash columns, masked positions,
-    # a ragged last 256-row tile when T = 4000, out written over x
+@pytest.mark.parametrize("dim,hc,n_heads,T,inplace", [(2048, 4, 3, 4096, False),
+                                                       (2048, 4, 3, 4000, True),
+                                                       (2048, 2, 3, 6100, False),
+                                                       (1024, 3, 3, 8192, True)])
+def test_forward_gate_partials_geometry(ge, dev, dim, hc, n_heads, T, inplace):
+    # smaller geometries that still take the fully fused path (gate sums in
+    # the projection's epilogue): 6 hash columns, 2 to 4 streams (the key
+    # tiles of each stream end in its own sums), masked positions, a
+    # ragged last 256-row tile when T = 4000 or 6100, out written over x
     import dataclasses
-    cfg = dataclasses.replace(synth.config("prefill"), dim=dim, n_heads=n_heads, T=T,
-                              mask_frac=0.2)
-    say("fused-gate forward", dim, n_heads, T, "in place" if inplace else "")
+    cfg = dataclasses.replace(synth.config("prefill"), dim=dim, hc_mult=hc, n_heads=n_heads,
+                              T=T, mask_frac=0.2)
+    say("fused-gate forward", dim, hc, n_heads, T, "in place" if inplace else "")
     wl = Workload(ge, cfg, dev)
+    assert ge.engram_gate_partials_supported(wl.g, T), "the case must take the fully fused path"
     ids_np = synth.token_ids(cfg, 1, T)
     ids = torch.from_numpy(ids_np).to(dev)
     x = synth.activations(cfg, T, dev).reshape(1, T, cfg.hc_mult, cfg.dim)
