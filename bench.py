@@ -177,12 +177,14 @@ def traffic_record(launch_flops_tokens: int, path: str = TRAFFIC_FILE):
     return rec.get("hbm_bytes_per_launch")
 
 
-def mfma_ceiling(dev, stream) -> dict:
+def mfma_ceiling(dev, stream, w) -> dict:
     """The part's matrix-core ceiling on this machine: the projection's MFMA back
     to back from registers (libengram_probe.so), 8 waves per CU, once with
     operands whose bits change every step (as in a GEMM) and once with zero
-    operands; TFLOP/s over event time, and the shader clock the loop ran at
-    (shader-clock ticks over constant-rate wall-clock ticks, median over
+    operands; then the same MFMA fed from LDS with the projection's own W
+    values and its per-k-step fragment reads, but no global traffic
+    (`lds_fed`).  TFLOP/s over event time, and the shader clock the loop ran
+    at (shader-clock ticks over constant-rate wall-clock ticks, median over
     workgroups)."""
     import ctypes as C
     import torch
@@ -195,6 +197,11 @@ def mfma_ceiling(dev, stream) -> dict:
     L.engram_probe_mfma.restype = C.c_int
     L.engram_probe_mfma.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int,
                                     C.c_void_p]
+    L.engram_probe_mfma_lds_flops.restype = C.c_double
+    L.engram_probe_mfma_lds_flops.argtypes = [C.c_int, C.c_int]
+    L.engram_probe_mfma_lds.restype = C.c_int
+    L.engram_probe_mfma_lds.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p, C.c_int,
+                                        C.c_int, C.c_void_p]
     L.engram_probe_wall_clock_hz.restype = C.c_int
     L.engram_probe_wall_clock_hz.argtypes = [C.POINTER(C.c_int64)]
     hz = C.c_int64(0)
@@ -210,10 +217,15 @@ def mfma_ceiling(dev, stream) -> dict:
     clocks = torch.empty(blocks * 2, dtype=torch.int64, device=dev)
     iters = 40000
     res = {}
-    for mode, zero in (("changing_operands", 0), ("zero_operands", 1)):
+    for mode, zero in (("changing_operands", 0), ("zero_operands", 1), ("lds_fed", -1)):
         def once():
-            r = L.engram_probe_mfma(seed.data_ptr(), sums.data_ptr(), clocks.data_ptr(), blocks,
-                                    iters, zero, stream.cuda_stream)
+            if zero < 0:
+                r = L.engram_probe_mfma_lds(w.data_ptr(), w.numel() * w.element_size(),
+                                            sums.data_ptr(), clocks.data_ptr(), blocks, iters,
+                                            stream.cuda_stream)
+            else:
+                r = L.engram_probe_mfma(seed.data_ptr(), sums.data_ptr(), clocks.data_ptr(),
+                                        blocks, iters, zero, stream.cuda_stream)
             if r != 0:
                 raise SystemExit("MFMA probe launch failed: %d" % r)
         once()
@@ -230,8 +242,9 @@ def mfma_ceiling(dev, stream) -> dict:
             c = clocks.cpu().view(-1, 2).double()
             ratios.append(float((c[:, 0] / c[:, 1]).median()) * hz.value / 1e9)
         t = sorted(times)[1]
-        res[mode] = {"tflops": round(L.engram_probe_mfma_flops(blocks, iters) / t / 1e12, 1),
-                     "clock_ghz": round(sorted(ratios)[1], 3)}
+        flops = (L.engram_probe_mfma_lds_flops(blocks, iters) if zero < 0
+                 else L.engram_probe_mfma_flops(blocks, iters))
+        res[mode] = {"tflops": round(flops / t / 1e12, 1), "clock_ghz": round(sorted(ratios)[1], 3)}
     return res
 
 
@@ -596,9 +609,10 @@ def main():
         del src, dst
 
     # the same projection against the part's measured matrix-core ceiling
-    ceil = mfma_ceiling(dev, stream)
+    ceil = mfma_ceiling(dev, stream, w)
     ceil["projection_frac_of_changing_operand_ceiling"] = round(
         achieved / ceil["changing_operands"]["tflops"], 4)
+    ceil["projection_frac_of_lds_fed_ceiling"] = round(achieved / ceil["lds_fed"]["tflops"], 4)
     rec["mfma_ceiling"] = ceil
 
     if not args.no_cpu_baseline:

@@ -8,7 +8,8 @@
 //   * zero: all-zero operands (the spec clock is reachable here).
 // Each workgroup also reads the shader clock and the constant-rate wall
 // clock at its start and end, so the host can report the clock the loop ran
-// at.  Measurement support for the bench; not part of the Engram path.
+// at.  A third loop feeds the same MFMA from LDS as the projection does
+// (below).  Measurement support for the bench; not part of the Engram path.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -65,6 +66,78 @@ mfma_loop(const uint4* __restrict__ seed, float* __restrict__ sums, uint64_t* __
     }
 }
 
+// The same MFMA fed the way the projection's k-loop feeds it, with no global
+// traffic: 128 KiB of the projection's own W values are staged in LDS once,
+// then per k-step of 8 MFMAs every wave reads the next k-step's 4 W and
+// (every other k-step) 2 A fragments, 16 bytes per lane, from LDS into
+// double-buffered operand registers.  This prices the fragment traffic
+// (LDS bandwidth and its power) that any LDS-staged GEMM tile of this shape
+// pays on top of the bare matrix-core work.
+constexpr int kLdsChunks = 8192;  // 16-byte chunks, 128 KiB
+
+__global__ void __launch_bounds__(kThreads, 1)
+mfma_lds_loop(const uint4* __restrict__ src, long src_chunks, float* __restrict__ sums,
+              uint64_t* __restrict__ clocks, int iters) {
+    __shared__ uint4 lds[kLdsChunks];
+    for (int i = threadIdx.x; i < kLdsChunks; i += kThreads)
+        lds[i] = src[((long)blockIdx.x * kLdsChunks + i) % src_chunks];
+    __syncthreads();
+    const int tid = blockIdx.x * kThreads + threadIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int base = (wave * 1024 + lane) & (kLdsChunks - 1);  // distinct 16-byte slots per lane
+    uint4 fw[2][4], fa[2][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fw[0][j] = lds[(base + 64 * j) & (kLdsChunks - 1)];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) fa[0][i] = lds[(base + 512 + 64 * i) & (kLdsChunks - 1)];
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
+    __syncthreads();
+    const uint64_t c0 = clock64(), w0 = wall_clock64();
+    int off = 0;
+    for (int it = 0; it < iters; it += 2) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            off = (off + 256) & 4095;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) fw[u ^ 1][j] = lds[(base + off + 64 * j) & (kLdsChunks - 1)];
+            if (u == 0)
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    fa[1][i] = lds[(base + off + 4096 + 64 * i) & (kLdsChunks - 1)];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        as_bf16x8(fw[u][j]), as_bf16x8(fa[u][i]), acc[j][i], 0, 0, 0);
+            if (u == 1) {
+                fa[0][0] = fa[1][0];
+                fa[0][1] = fa[1][1];
+            }
+        }
+    }
+    __syncthreads();
+    const uint64_t c1 = clock64(), w1 = wall_clock64();
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) s += acc[j][i][v];
+    sums[tid] = s;
+    if (threadIdx.x == 0) {
+        clocks[2 * blockIdx.x] = c1 - c0;
+        clocks[2 * blockIdx.x + 1] = w1 - w0;
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -82,6 +155,24 @@ int engram_probe_mfma(const void* seed, float* sums, uint64_t* clocks, int block
     if (!seed || !sums || !clocks || blocks < 1 || iters < 1) return (int)hipErrorInvalidValue;
     mfma_loop<<<dim3(blocks), dim3(kThreads), 0, stream>>>(
         reinterpret_cast<const uint4*>(seed), sums, clocks, iters, zero);
+    return (int)hipGetLastError();
+}
+
+// Flops of one mfma_lds_loop call: blocks * 8 waves * iters k-steps of 8
+// MFMAs of 32x32x16 (iters even).
+double engram_probe_mfma_lds_flops(int blocks, int iters) {
+    return (double)blocks * (kThreads / 64) * (double)iters * 8 * 2.0 * 32 * 32 * 16;
+}
+
+// src: device, src_bytes of bf16 operand values (at least 16 bytes, a
+// multiple of 16); sums and clocks as for engram_probe_mfma.
+int engram_probe_mfma_lds(const void* src, size_t src_bytes, float* sums, uint64_t* clocks,
+                          int blocks, int iters, hipStream_t stream) {
+    if (!src || src_bytes < 16 || src_bytes % 16 || !sums || !clocks || blocks < 1 || iters < 2 ||
+        iters % 2)
+        return (int)hipErrorInvalidValue;
+    mfma_lds_loop<<<dim3(blocks), dim3(kThreads), 0, stream>>>(
+        reinterpret_cast<const uint4*>(src), (long)(src_bytes / 16), sums, clocks, iters);
     return (int)hipGetLastError();
 }
 
