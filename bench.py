@@ -316,7 +316,7 @@ def summarize(stats_dir, fetch_dir, write_dir):
              "# engram_wkv_gate_partials = prep_kernel + wkv_gathered_256<3, true, true> + wkv_gathered_128<L>",
              "# (prep_kernel and wkv_gathered_128 also run in the engram_wkv_gathered calls bench times);",
              "# averages include every call (warm-up and cold-clock launches too);",
-             "# mfma_loop is the bench's matrix-core ceiling probe (libengram_probe.so).",
+             "# mfma_loop and mfma_lds_loop are the bench's matrix-core ceiling probes (libengram_probe.so).",
              "",
              "%-34s %7s %12s %12s %12s %7s" % ("kernel", "calls", "avg_ns", "min_ns", "max_ns", "pct")]
     for r in rows:
