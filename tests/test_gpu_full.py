@@ -140,6 +140,56 @@ def test_prefill_full(ge, dev):
     say("   end to end", st)
 
 
+# ------------------------------------------------------------------ two sequences, state carried
+# The fully fused prefill with two sequences at the full geometry, after a
+# short first chunk (decode-sized tiles) has filled the hash state: the first
+# positions of each sequence reach into the state, and every position's hash
+# ids, the state after the call, and the outputs at sampled positions of both
+# sequences (the state-dependent first positions among them) are checked.
+def test_prefill_two_sequences_after_a_chunk(ge, dev):
+    import dataclasses
+    B, T1, T2 = 2, 5, 2048
+    cfg = dataclasses.replace(synth.config("prefill"), B=B, T=T2)
+    say("two-sequence prefill: building tables")
+    wl = Workload(ge, cfg, dev)
+    assert ge.engram_gate_partials_supported(wl.g, B * T2)
+    ids1 = synth.token_ids(cfg, B, T1, name="chunk1")
+    ids2 = synth.token_ids(cfg, B, T2, name="chunk2")
+    layer = ge.EngramLayer(wl.g, wl.tables, wl.table, wl.scales, wl.w, wl.q, wl.k)
+    state = torch.full((B, cfg.max_ngram_size - 1), cfg.pad_id, dtype=torch.int32, device=dev)
+    x1 = synth.activations(cfg, B * T1, dev, name="chunk1x").reshape(B, T1, cfg.hc_mult, cfg.dim)
+    layer.forward(x1, torch.from_numpy(ids1).to(dev), state=state)
+    probe = state.clone()
+    got_h = ge.engram_hash(wl.g, wl.tables, torch.from_numpy(ids2).to(dev), state=probe)
+    x = synth.activations(cfg, B * T2, dev, name="chunk2x").reshape(B, T2, cfg.hc_mult, cfg.dim)
+    gate = torch.empty((B, T2, cfg.hc_mult), dtype=torch.float32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = layer.forward(x, torch.from_numpy(ids2).to(dev), state=state, gate=gate, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    ost = oracle.HashState(B, T1 + T2 + 4)
+    oracle.hash_ids(wl.t, wl.geom, ost, ids1)
+    ref_h = oracle.hash_ids(wl.t, wl.geom, ost, ids2)
+    assert np.array_equal(got_h.cpu().numpy(), ref_h)
+    assert torch.equal(state, probe)
+    assert np.array_equal(state.cpu().numpy(), wl.t["token_map"][ids2[:, -2:]])
+    say("two-sequence prefill: oracle at sampled positions")
+    sel = [(b, p) for b in range(B) for p in _sample_positions(T2, extra=(3, 255, 256), n=20, seed=b)]
+    bb = np.array([b for b, _ in sel])
+    pp = np.array([p for _, p in sel])
+    tab, sc, inv = wl.host_rows(ref_h[bb, pp])
+    rows = oracle.embed_rows(tab, sc, inv.reshape(-1)).reshape(len(sel), -1)
+    kv = oracle.linear(rows, bits(wl.w))
+    xb = bits(x)[bb, pp]
+    r_out, r_gate, r_a = oracle.gate_and_add(xb, kv, bits(wl.q), bits(wl.k), cfg.norm_eps)
+    ref = dict(rows=rows, kv=kv, out=r_out, gate=r_gate, a=r_a)
+    st = _check_tokens(ref, bits(out)[bb, pp], gate.cpu().numpy()[bb, pp], xb, wl,
+                       min_tight=PREFILL_FLOORS["gate_tight"],
+                       max_rel=PREFILL_FLOORS["gate_max_rel"],
+                       max_frac_beyond=PREFILL_FLOORS["out_beyond_2ulp"])
+    say("   end to end (%d positions)" % len(sel), st)
+
+
 # ------------------------------------------------------------------ mid-sized batches
 # Between decode-sized (<= 256 positions) and prefill-sized batches the
 # forward runs the hash into the fused gathered projection in 256-wide tiles,
