@@ -188,9 +188,9 @@ def mfma_ceiling(dev, stream, w) -> dict:
     workgroups)."""
     import ctypes as C
     import torch
-    path = os.path.join(ROOT, "gram_memory_layer_amd", "libengram_probe.so")
+    path = os.path.join(ROOT, "bench_probe", "libengram_probe.so")
     if not os.path.exists(path):
-        raise SystemExit("libengram_probe.so is not built; run `python -m gram_memory_layer_amd.build`")
+        raise SystemExit("libengram_probe.so is not built; run `python -m bench_probe.build`")
     L = C.CDLL(path)
     L.engram_probe_mfma_flops.restype = C.c_double
     L.engram_probe_mfma_flops.argtypes = [C.c_int, C.c_int]

@@ -3,8 +3,7 @@
     python -m gram_memory_layer_amd.build
 
 Each csrc/*.hip file is compiled to an object in parallel, then linked into
-gram_memory_layer_amd/libengram.so; probe/mfma_peak.hip (the bench's MFMA
-ceiling probe) becomes libengram_probe.so.  Always rebuilds.
+gram_memory_layer_amd/libengram.so.  Always rebuilds.
 """
 from __future__ import annotations
 
@@ -19,9 +18,6 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libengram.so")
-# measurement support for the bench (the MFMA ceiling probe), not the path
-PROBE_SRC = os.path.join(HERE, "probe", "mfma_peak.hip")
-PROBE_OUT = os.path.join(HERE, "libengram_probe.so")
 OBJDIR = os.path.join(HERE, "_build")
 
 ARCH = "gfx950"
@@ -61,14 +57,11 @@ def _link(objs, out: str) -> None:
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
     srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + 1)) as ex:
-        probe = ex.submit(_compile, PROBE_SRC)
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
-        probe_obj = probe.result()
     _link(objs, OUT)
-    _link([probe_obj], PROBE_OUT)
     if verbose:
-        print("built", OUT, "and", PROBE_OUT)
+        print("built", OUT)
     return OUT
 
 

@@ -31,7 +31,8 @@ def test_probe_library_loads_and_refuses_bad_arguments():
     # the bench's MFMA ceiling probe: a library of its own, no Engram symbols
     import ctypes as C
     import os
-    path = os.path.join(os.path.dirname(ge.__file__), "libengram_probe.so")
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                        "bench_probe", "libengram_probe.so")
     lib = C.CDLL(path)
     for n in ("engram_probe_mfma", "engram_probe_mfma_flops", "engram_probe_wall_clock_hz"):
         assert hasattr(lib, n), n
