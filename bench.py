@@ -108,20 +108,39 @@ def summarize_counters(pmc_dir, name, rocprof_args):
     --pmc run of the prefill bench, with the derived clock and matrix-core
     busy share where GRBM_GUI_ACTIVE and SQ_VALU_MFMA_BUSY_CYCLES are present
     (GUI_ACTIVE is summed over the 8 XCDs; the busy cycles over the 1024
-    SIMDs)."""
+    SIMDs).  GUI_ACTIVE also counts a fixed number of cycles per dispatch
+    beyond the kernel's own run; that part is fitted over the run's short
+    dispatches (every kernel under 120 us: cycles per XCD = rate * duration
+    + fixed) and taken off before the clock is derived."""
+    import numpy as np
     per = {}
+    fit_x, fit_y = [], []
     for r in _csv(pmc_dir, "counter_collection.csv"):
+        dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        if r["Counter_Name"] == "GRBM_GUI_ACTIVE" and dur < 120e3:
+            fit_x.append(dur / 1e3)
+            fit_y.append(float(r["Counter_Value"]) / N_XCD_COUNT)
         if "engram::" not in r["Kernel_Name"]:
             continue
         k = short_name(r["Kernel_Name"])
         d = per.setdefault(k, {"_dur": {}})
         d.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
-        d["_dur"][r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        d["_dur"][r["Dispatch_Id"]] = dur
+    fixed = 0.0
+    if len(fit_x) >= 2:
+        A = np.vstack([np.array(fit_x), np.ones(len(fit_x))]).T
+        rate, fixed = np.linalg.lstsq(A, np.array(fit_y), rcond=None)[0]
     lines = ["# rocprofv3 counters per dispatch (mean over dispatches): Engram prefill bench",
              "# command (repository root = <repo>):",
              "#   cd /tmp && export TMPDIR=/tmp && rocprofv3 %s --output-format csv -d <out> "
              "-o <name> -- python3 <repo>/bench.py --no-cpu-baseline --steps 5 --warmup 3"
-             % rocprof_args, ""]
+             % rocprof_args]
+    if fixed:
+        lines.append("# GRBM_GUI_ACTIVE per XCD over the %d dispatches under 120 us fits %.0f "
+                     "cycles per us + %.0f per dispatch;" % (len(fit_x), rate, fixed))
+        lines.append("#   the clock below is (GUI_ACTIVE per XCD - %.0f) / median time, and the "
+                     "matrix-core busy share is over those cycles" % fixed)
+    lines.append("")
     for k in sorted(per):
         d = per[k]
         durs = sorted(d.pop("_dur").values())
@@ -129,12 +148,13 @@ def summarize_counters(pmc_dir, name, rocprof_args):
         lines.append("%s  (%d dispatches, median %.1f us)" % (k, len(durs), med / 1e3))
         for c in sorted(d):
             lines.append("    %-28s %14.4g" % (c, sum(d[c]) / len(d[c])))
-        # GRBM_GUI_ACTIVE carries a fixed cost of roughly 17k cycles per XCD
-        # per dispatch: a clock derived from it means something only for
-        # kernels that run much longer than that (50 us and up)
+        # with the fixed part taken off, a clock derived from GUI_ACTIVE means
+        # something only for kernels that run much longer than that part
+        # (50 us and up)
         if "GRBM_GUI_ACTIVE" in d and med >= 50e3:
-            gui = sum(d["GRBM_GUI_ACTIVE"]) / len(d["GRBM_GUI_ACTIVE"]) / N_XCD_COUNT
-            lines.append("    clock (GUI_ACTIVE per XCD / median time)   %.2f GHz" % (gui / med))
+            gui = sum(d["GRBM_GUI_ACTIVE"]) / len(d["GRBM_GUI_ACTIVE"]) / N_XCD_COUNT - fixed
+            lines.append("    clock (GUI_ACTIVE per XCD less fixed / median time)  %.2f GHz"
+                         % (gui / med))
             if "SQ_VALU_MFMA_BUSY_CYCLES" in d:
                 busy = sum(d["SQ_VALU_MFMA_BUSY_CYCLES"]) / len(d["SQ_VALU_MFMA_BUSY_CYCLES"])
                 lines.append("    matrix cores busy (busy / SIMDs / cycles)  %.1f %%"
