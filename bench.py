@@ -391,6 +391,7 @@ def summarize(stats_dir, fetch_dir, write_dir):
         "\n".join(lines) + "\n")
     rec = {"kernel": "engram_wkv_gate_partials (" + " + ".join(FUSED_KERNELS) + ")",
            "workload": "prefill T=4096 dim 5120 hc 4", "tokens": tokens,
+           "summary": "engram_prefill_T4096_traffic.txt (the rocprofv3 commands in its header)",
            "source_digest": kernel_source_digest(),
            "fetch_bytes_per_launch": int(total["fetch"]),
            "write_bytes_per_launch": int(total["write"]),
@@ -438,6 +439,7 @@ def summarize_decode_traffic(fetch_dir, write_dir):
         "\n".join(lines) + "\n")
     rec = {"kernel": "engram_wkv_gathered at M = 64 (" + " + ".join(DECODE_KERNELS) + ")",
            "workload": "decode B=64 dim 5120 hc 4", "tokens": 64,
+           "summary": "engram_decode_B64_traffic.txt (the rocprofv3 commands in its header)",
            "source_digest": kernel_source_digest(),
            "fetch_bytes_per_launch": int(total["fetch"]),
            "write_bytes_per_launch": int(total["write"]),
