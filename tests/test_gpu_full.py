@@ -190,6 +190,48 @@ def test_prefill_two_sequences_after_a_chunk(ge, dev):
     say("   end to end (%d positions)" % len(sel), st)
 
 
+# ------------------------------------------------------------------ routing boundaries
+# The forward picks its kernels by the batch size: up to 256 positions the
+# fused projection in 64-wide tiles, then 256-wide tiles with the gate after
+# the full kv, and from 1,281 positions at this geometry (every compute unit
+# two 256x256 tiles or more) the fully fused path with the gate's sums in
+# the projection.  Both sides of each boundary at the full geometry: every
+# position at 256 and 257, sampled positions (the tile edges among them) at
+# 1,280 and 1,281; hash ids and the state everywhere.
+def test_forward_routing_boundaries(ge, dev):
+    import dataclasses
+    cfg0 = dataclasses.replace(synth.config("prefill"), B=1, T=256)
+    say("routing boundaries: building tables")
+    wl = Workload(ge, cfg0, dev)
+    assert not ge.engram_gate_partials_supported(wl.g, 1280)
+    assert ge.engram_gate_partials_supported(wl.g, 1281)
+    layer = ge.EngramLayer(wl.g, wl.tables, wl.table, wl.scales, wl.w, wl.q, wl.k)
+    for T in (256, 257, 1280, 1281):
+        cfg = dataclasses.replace(cfg0, T=T)
+        say("routing boundary T=%d" % T)
+        ids_np = synth.token_ids(cfg, 1, T, name="route%d" % T)
+        x = synth.activations(cfg, T, dev, name="routex%d" % T).reshape(1, T, cfg.hc_mult, cfg.dim)
+        state = torch.full((1, cfg.max_ngram_size - 1), cfg.pad_id, dtype=torch.int32,
+                           device=dev)
+        gate = torch.empty((1, T, cfg.hc_mult), dtype=torch.float32, device=dev)
+        err = torch.zeros(1, dtype=torch.int32, device=dev)
+        out = layer.forward(x, torch.from_numpy(ids_np).to(dev), state=state, gate=gate, err=err)
+        hid = ge.engram_hash(wl.g, wl.tables, torch.from_numpy(ids_np).to(dev))
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
+        ref_h = oracle.hash_ids(wl.t, wl.geom, oracle.HashState(1, T + 4), ids_np)
+        assert np.array_equal(hid.cpu().numpy(), ref_h)
+        assert np.array_equal(state.cpu().numpy(), wl.t["token_map"][ids_np[:, -2:]])
+        pos = (np.arange(T) if T <= 257 else
+               _sample_positions(T, extra=(255, 256, 1023, 1024, 1279, 1280), n=40, seed=T))
+        ref = _oracle_tokens(wl, ids_np[0], pos, bits(x)[0, pos])
+        st = _check_tokens(ref, bits(out)[0, pos], gate.cpu().numpy()[0, pos], bits(x)[0, pos],
+                           wl, min_tight=MID_FLOORS["gate_tight"],
+                           max_rel=MID_FLOORS["gate_max_rel"],
+                           max_frac_beyond=MID_FLOORS["out_beyond_2ulp"])
+        say("   end to end (%d positions)" % len(pos), st)
+
+
 # ------------------------------------------------------------------ mid-sized batches
 # Between decode-sized (<= 256 positions) and prefill-sized batches the
 # forward runs the hash into the fused gathered projection in 256-wide tiles,
