@@ -129,8 +129,8 @@ engram_status forward_launch(const engram_geometry* g, const engram_hash_tables*
             gp.m_live = m_live;
             gp.rowmap = rowmap;
         }
-        hipError_t e = engram::launch_hash_prep(gg, *t, state, ids, B, T, scales, q, k, rows, err,
-                                                s, mask, live_idx, rowmap, m_live);
+        hipError_t e = engram::launch_hash_prep(gg, *t, state, ids, B, T, table, scales, q, k,
+                                                rows, err, s, mask, live_idx, rowmap, m_live);
         if (e == hipSuccess)
             e = engram::launch_wkv_gate_partials(gg, nullptr, table, scales, w, n_tok, gp, v, rows,
                                                  err, s, /*prepared=*/true);
@@ -141,8 +141,8 @@ engram_status forward_launch(const engram_geometry* g, const engram_hash_tables*
     }
     hipError_t e;
     if (fused) {
-        e = engram::launch_hash_prep(gg, *t, state, ids, B, T, scales, nullptr, nullptr, rows, err,
-                                     s);
+        e = engram::launch_hash_prep(gg, *t, state, ids, B, T, table, scales, nullptr, nullptr,
+                                     rows, err, s);
         if (e == hipSuccess)
             e = engram::launch_wkv_gathered(gg, nullptr, table, scales, w, n_tok, kv, rows, err, s,
                                             /*prepared=*/true);
@@ -423,7 +423,7 @@ engram_status engram_forward_hashed(const engram_geometry* g, const uint8_t* tab
             gp.rowmap = rowmap;
         }
         if (e == hipSuccess)
-            e = engram::launch_prep_scratch(gg, hash_ids, scales, n_tok, rows, err, s, q, k,
+            e = engram::launch_prep_scratch(gg, hash_ids, table, scales, n_tok, rows, err, s, q, k,
                                             mask ? live_idx : nullptr, mask ? m_live : nullptr);
         if (e == hipSuccess)
             e = engram::launch_wkv_gate_partials(gg, nullptr, table, scales, w, n_tok, gp, v, rows,

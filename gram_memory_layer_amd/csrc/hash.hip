@@ -19,8 +19,9 @@
 // workgroups.
 //
 // Two output forms: hash ids [M][n_cols] (column fastest), or the fused
-// projections' row offsets and scales [n_cols][m_pad] (row fastest, with
-// q*k beside them when asked).
+// projections' rows and scales [n_cols][m_pad] (row fastest: each item
+// copies its table row's 64 codes there, or for decode-sized batches writes
+// the row's table offset, with q*k beside them when asked).
 #include "internal.h"
 
 namespace engram {
@@ -61,9 +62,11 @@ struct HashArgs {
     int n_body, seq_per_head;
     // hash-id form
     int32_t* hash_ids;
-    // offsets-and-scales form
+    // rows-and-scales form (arows, or aoff for decode-sized batches)
+    const uint8_t* table;
     const uint8_t* scales;
     int64_t m_pad;
+    uint8_t* arows;
     uint32_t* aoff;
     float2* scl;
     const uint16_t* q;
@@ -102,24 +105,53 @@ __device__ __forceinline__ int32_t hash_at(const HashArgs& a, int b, int t, int 
     return -1;
 }
 
+// A zero row (or a bad row offset) and zero scales at projection row r of
+// column col: a bad id, or a padding row the projection reads past the last
+// position.
+__device__ __forceinline__ void zero_row(const HashArgs& a, int64_t r, int col) {
+    const int64_t i = (int64_t)col * a.m_pad + r;
+    if (a.arows) {
+        uint4* dst = reinterpret_cast<uint4*>(a.arows + i * 64);
+        const uint4 z = make_uint4(0, 0, 0, 0);
+        dst[0] = z;
+        dst[1] = z;
+        dst[2] = z;
+        dst[3] = z;
+    } else {
+        a.aoff[i] = kBadRowOffset;
+    }
+    a.scl[i] = make_float2(0.0f, 0.0f);
+}
+
 // Store the result of item (position m, column col) in the output form.  In
-// the offsets-and-scales form a hash outside the table is also a bad row, as
+// the rows-and-scales form a hash outside the table is also a bad row, as
 // it is when the ids pass through memory to the projection; with compacted
 // rows a masked position is not placed (and its row never read).
-// The row offset and scales of hash id `id` at projection row r.
+// The table row (or its offset) and scales of hash id `id` at projection
+// row r (the row's loads and the scales' go out together).
 __device__ __forceinline__ void place(const HashArgs& a, int64_t r, int col, int32_t id,
                                       uint32_t* bad) {
-    uint32_t off = kBadRowOffset;
-    float2 sc = make_float2(0.0f, 0.0f);
-    if (id >= 0) {
-        off = (uint32_t)id * 64u;
-        sc = make_float2(e8m0_scale(a.scales[2 * (int64_t)id]),
-                         e8m0_scale(a.scales[2 * (int64_t)id + 1]));
-    } else {
+    if (id < 0) {
         *bad |= ENGRAM_ERRBIT_ROW;
+        zero_row(a, r, col);
+        return;
     }
     const int64_t i = (int64_t)col * a.m_pad + r;
-    a.aoff[i] = off;
+    const float2 sc = make_float2(e8m0_scale(a.scales[2 * (int64_t)id]),
+                                  e8m0_scale(a.scales[2 * (int64_t)id + 1]));
+    if (a.arows) {
+        // four named values, all loads before the stores (a local array of
+        // them ends up in scratch memory)
+        const uint4* src = reinterpret_cast<const uint4*>(a.table + (int64_t)id * 64);
+        const uint4 v0 = src[0], v1 = src[1], v2 = src[2], v3 = src[3];
+        uint4* dst = reinterpret_cast<uint4*>(a.arows + i * 64);
+        dst[0] = v0;
+        dst[1] = v1;
+        dst[2] = v2;
+        dst[3] = v3;
+    } else {
+        a.aoff[i] = (uint32_t)id * 64u;
+    }
     a.scl[i] = sc;
 }
 
@@ -193,8 +225,7 @@ __device__ __forceinline__ void body_fused(const HashArgs& a, int body_from, uin
         const int64_t tot = pre + blk;
         const int64_t r = tot + tid;
         if (r < (tot + 255) / 256 * 256) {
-            a.aoff[(int64_t)col * a.m_pad + r] = kBadRowOffset;
-            a.scl[(int64_t)col * a.m_pad + r] = make_float2(0.0f, 0.0f);
+            zero_row(a, r, col);
             if (col == 0) a.rowmap_out[r] = (int32_t)M;
         }
         if (col == 0 && tid == 0) *a.m_live_out = (int)tot;
@@ -237,10 +268,7 @@ __device__ __forceinline__ void hash_work(const HashArgs& a) {
             m = i - (int64_t)col * a.m_pad;
             // row m holds no position from the row count on (M, or the live
             // count when compacted): a bad row
-            if (m >= (a.live_idx ? (int64_t)*a.m_live : M)) {
-                a.aoff[i] = kBadRowOffset;
-                a.scl[i] = make_float2(0.0f, 0.0f);
-            }
+            if (m >= (a.live_idx ? (int64_t)*a.m_live : M)) zero_row(a, m, col);
             if (m >= M) return;
         } else {  // columns fastest
             if (i >= M * a.n_cols) return;
@@ -368,7 +396,8 @@ int head_blocks(const Geom& g, int B, int T, int* seq_per_head) {
 }  // namespace
 
 hipError_t launch_hash_prep(const Geom& g, const engram_hash_tables& t, int32_t* state,
-                            const int32_t* ids, int B, int T, const uint8_t* scales,
+                            const int32_t* ids, int B, int T, const uint8_t* table,
+                            const uint8_t* scales,
                             const uint16_t* q, const uint16_t* k, void* scratch, uint32_t* err,
                             hipStream_t s, const uint8_t* mask, int32_t* live_idx,
                             int32_t* rowmap, int* m_live) {
@@ -398,8 +427,10 @@ hipError_t launch_hash_prep(const Geom& g, const engram_hash_tables& t, int32_t*
             a.m_live = m_live;
         }
     }
+    a.table = table;
     a.scales = scales;
     a.m_pad = gs.m_pad;
+    a.arows = gs.arows;
     a.aoff = gs.aoff;
     a.scl = gs.scl;
     a.q = q;

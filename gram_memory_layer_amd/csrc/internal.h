@@ -81,14 +81,24 @@ struct GatePartials {
 hipError_t launch_live_rows(const uint8_t* mask, int64_t M, int64_t m_pad, int32_t* live_idx,
                             int32_t* rowmap, int* m_live, hipStream_t s);
 
-// Scratch of the fused projections: per (hash column c, padded row m) the
-// table byte offset of row hash_ids[m][c] (kBadRowOffset, past any table,
-// for a bad id or a padding row: the buffer load then reads zeros) and the
-// row's two block scales as fp32; then q*k in fp32 per (stream, feature).
+// Scratch of the fused projections, per (hash column c, padded row m):
+//  * batches of more than 256 positions (256- and 128-wide tiles, each A row
+//    read by many workgroups): the 64 fp8 codes of table row hash_ids[m][c],
+//    copied there by the hash or prep kernel (zeros for a bad id and for the
+//    padding rows past the last position), so that k-tile c of rows m0.. is
+//    one contiguous run at a computed address;
+//  * decode-sized batches (64-wide tiles): the table byte offset of that row
+//    instead (kBadRowOffset, past any table, for a bad id or a padding row:
+//    the buffer load then reads zeros); the projection fetches the row itself,
+//    beside its weight stream;
+// then the row's two block scales as fp32 (zero for a zero row), and q*k in
+// fp32 per (stream, feature).
 constexpr uint32_t kBadRowOffset = 0xFFFFFFC0u;
+constexpr int64_t kOffsetRowsMax = 256;  // batches up to this size use row offsets
 __host__ __device__ inline int64_t padded_rows(int64_t M) { return (M + 255) / 256 * 256; }
 struct GatheredScratch {
-    uint32_t* aoff;  // [n_cols][m_pad]
+    uint8_t* arows;  // [n_cols][m_pad][64], when M > kOffsetRowsMax
+    uint32_t* aoff;  // [n_cols][m_pad], when M <= kOffsetRowsMax
     float2* scl;     // [n_cols][m_pad]
     float* wqk;      // [hc * dim]
     int64_t m_pad;
@@ -105,18 +115,19 @@ __device__ __forceinline__ float e8m0_scale(uint32_t c) {
 }
 
 // Stage 1 straight into the fused projections' scratch (the hash ids
-// themselves are not written): for every position and hash column, the row
-// offset and scales; q*k as well when q is given; the state updated as in
-// launch_hash.
+// themselves are not written): for every position and hash column, the
+// table row's codes (or its offset) and scales; q*k as well when q is given;
+// the state updated as in launch_hash.
 // With a mask, the live positions are packed in order: live_idx, rowmap and
 // *m_live are written as by launch_live_rows (by that kernel first, or, for
 // short single sequences, by the hash kernel itself), live positions go to
 // their compact rows, masked ones are hashed (their token and hash checks
 // still flag) but not placed, and the compact rows past the live count that
-// the projection reads are bad rows.
+// the projection reads are zero (or bad) rows.
 constexpr int64_t kFusedCompactionMax = 32768;
 hipError_t launch_hash_prep(const Geom& g, const engram_hash_tables& t, int32_t* state,
-                            const int32_t* ids, int B, int T, const uint8_t* scales,
+                            const int32_t* ids, int B, int T, const uint8_t* table,
+                            const uint8_t* scales,
                             const uint16_t* q, const uint16_t* k, void* scratch, uint32_t* err,
                             hipStream_t s, const uint8_t* mask = nullptr,
                             int32_t* live_idx = nullptr, int32_t* rowmap = nullptr,
@@ -126,8 +137,8 @@ hipError_t launch_hash_prep(const Geom& g, const engram_hash_tables& t, int32_t*
 // stage calls' own prep does); with q, also q*k; with live_idx and m_live
 // (from launch_live_rows), live positions at their compact rows as in
 // launch_hash_prep.
-hipError_t launch_prep_scratch(const Geom& g, const int32_t* hash_ids, const uint8_t* scales,
-                               int64_t M, void* scratch, uint32_t* err, hipStream_t s,
+hipError_t launch_prep_scratch(const Geom& g, const int32_t* hash_ids, const uint8_t* table,
+                               const uint8_t* scales, int64_t M, void* scratch, uint32_t* err, hipStream_t s,
                                const uint16_t* q = nullptr, const uint16_t* k = nullptr,
                                const int32_t* live_idx = nullptr, const int* m_live = nullptr);
 
@@ -137,7 +148,7 @@ int cu_count();
 // projection straight from hash ids (rows gathered as the GEMM's A operand)
 bool gathered_supported(const Geom& g, int64_t M);
 size_t gathered_scratch_bytes(const Geom& g, int64_t M);
-// prepared: the scratch already holds the offsets and scales (launch_hash_prep)
+// prepared: the scratch already holds the rows and scales (launch_hash_prep)
 hipError_t launch_wkv_gathered(const Geom& g, const int32_t* hash_ids, const uint8_t* table,
                                const uint8_t* scales, const uint16_t* w, int64_t M, uint16_t* kv,
                                void* scratch, uint32_t* err, hipStream_t s,

@@ -11,13 +11,19 @@
 // A this halves A's LDS writes and reads, drops the rows round trip through
 // HBM, and leaves room for a 3-stage ring (loads two k-tiles ahead).
 //
-// A small prep kernel first turns the hash ids into column-major arrays
-//   aoff[c][m]  byte offset of row hash_ids[m][c] in the table (or a value
-//               past the table for a bad id or a padding row: reads as 0),
-//   scl[c][m]   the row's two 32-block scales 2^(s-127) as fp32,
-// so that the projection's per-k-tile fetches are contiguous and it does no
-// id checks or scale decoding in its inner loop.  (The forward skips it: its
-// hash kernel writes these arrays directly.)
+// A small prep kernel first regroups the rows per hash column:
+//   arows[c][m]  the 64 fp8 codes of table row hash_ids[m][c] (zeros for a
+//                bad id or a padding row), for batches of more than 256
+//                positions: the 256- and 128-wide tiles then fetch each
+//                k-tile's rows as contiguous runs at computed addresses (no
+//                row offsets to load first, two rows per cache line);
+//   aoff[c][m]   for decode-sized batches, the row's byte offset in the table
+//                instead (past the table for a bad id or a padding row: reads
+//                as 0): the 64-wide tiles fetch the rows themselves, beside
+//                the weight stream, rather than wait for a copy;
+//   scl[c][m]    the row's two 32-block scales 2^(s-127) as fp32,
+// so that the projection does no id checks or scale decoding in its inner
+// loop.  (The forward skips it: its hash kernel writes these arrays.)
 //
 // LDS: each of the three ring stages is made of 1 KiB blocks (one buffer DMA
 // instruction each: 16 fp8 A rows, or 8 W rows of 128 bytes) plus 256 bytes
@@ -36,7 +42,6 @@ namespace {
 
 constexpr int G_NS = 3;                   // stages in the LDS ring
 constexpr int G_GROUP_M = 4;              // M-tiles per group in the tile order
-constexpr uint32_t kBadRow = kBadRowOffset;  // past any table: the DMA reads zeros
 
 // 16-byte slot of logical chunk c (0..3) in a 64-byte LDS row.  A fragment
 // read is one 16-byte chunk of 32 consecutive rows; the XOR term is a
@@ -49,12 +54,15 @@ __device__ __forceinline__ int slot64(int row, int c) {
 
 
 // One thread per (column c, padded row m), m fastest.  Padding rows m >= M
-// get kBadRow and zero scales.  With q and k given, the threads also write
-// wqk = q*k in fp32 (exact: two 8-bit significands) for the gate partials.
+// get zero codes (or a bad offset) and zero scales.  With q and k given, the
+// threads also write wqk = q*k in fp32 (exact: two 8-bit significands) for
+// the gate partials.
 __global__ void __launch_bounds__(256) prep_kernel(const int32_t* __restrict__ hash_ids,
                                                    int n_cols, int64_t M, int64_t m_pad,
+                                                   const uint8_t* __restrict__ table,
                                                    const uint8_t* __restrict__ scales,
-                                                   int64_t num_rows, uint32_t* __restrict__ aoff,
+                                                   int64_t num_rows, uint8_t* __restrict__ arows,
+                                                   uint32_t* __restrict__ aoff,
                                                    float2* __restrict__ scl,
                                                    uint32_t* __restrict__ err,
                                                    const uint16_t* __restrict__ q,
@@ -69,12 +77,24 @@ __global__ void __launch_bounds__(256) prep_kernel(const int32_t* __restrict__ h
     if (i >= (int64_t)n_cols * m_pad) return;
     const int c = (int)(i / m_pad);
     const int64_t m = i - (int64_t)c * m_pad;
+    const uint4 zero = make_uint4(0, 0, 0, 0);
     // compacted rows: row r holds no position from the live count on
     if (live_idx && m >= *m_live) {
-        aoff[i] = kBadRow;
+        if (arows) {
+            uint4* dst = reinterpret_cast<uint4*>(arows + i * 64);
+            dst[0] = zero;
+            dst[1] = zero;
+            dst[2] = zero;
+            dst[3] = zero;
+        } else {
+            aoff[i] = kBadRowOffset;
+        }
         scl[i] = make_float2(0.0f, 0.0f);
     }
-    uint32_t off = kBadRow;
+    // the row as four named values (a local array of them ends up in
+    // scratch memory)
+    uint4 v0 = zero, v1 = zero, v2 = zero, v3 = zero;
+    uint32_t off = kBadRowOffset;
     float2 sc = make_float2(0.0f, 0.0f);
     int64_t r = m;  // the projection row of position m
     if (m < M) {
@@ -84,6 +104,13 @@ __global__ void __launch_bounds__(256) prep_kernel(const int32_t* __restrict__ h
         }
         const int32_t id = hash_ids[m * n_cols + c];
         if (id >= 0 && id < num_rows) {
+            if (arows) {
+                const uint4* src = reinterpret_cast<const uint4*>(table + (int64_t)id * 64);
+                v0 = src[0];
+                v1 = src[1];
+                v2 = src[2];
+                v3 = src[3];
+            }
             off = (uint32_t)id * 64u;
             sc = make_float2(e8m0_scale(scales[2 * (int64_t)id]),
                              e8m0_scale(scales[2 * (int64_t)id + 1]));
@@ -93,8 +120,17 @@ __global__ void __launch_bounds__(256) prep_kernel(const int32_t* __restrict__ h
     } else if (live_idx) {
         return;  // (padding rows are filled above, as rows past the live count)
     }
-    aoff[(int64_t)c * m_pad + r] = off;
-    scl[(int64_t)c * m_pad + r] = sc;
+    const int64_t o = (int64_t)c * m_pad + r;
+    if (arows) {
+        uint4* dst = reinterpret_cast<uint4*>(arows + o * 64);
+        dst[0] = v0;
+        dst[1] = v1;
+        dst[2] = v2;
+        dst[3] = v3;
+    } else {
+        aoff[o] = off;
+    }
+    scl[o] = sc;
 }
 
 // Ring hand-over: wait until at most N of this wave's vector loads are in
@@ -112,6 +148,15 @@ __device__ __forceinline__ void handover() {
 template <int V>
 using IC = std::integral_constant<int, V>;
 
+// Where a projection finds its fp8 A rows: the rows copied per hash column
+// (256- and 128-wide tiles; aoff null), or the table itself at the row
+// offsets aoff (64-wide tiles).  Buffer loads past src_bytes read zeros.
+struct ASource {
+    const uint8_t* src;    // arows [n_cols][m_pad][64], or the table
+    const uint32_t* aoff;  // [n_cols][m_pad] table byte offsets, or null
+    uint32_t src_bytes;
+};
+
 // One workgroup's work.
 //   P = false: one output tile; L is the number of k-tiles after the steady
 //     loop (nk <= 2 ? nk : 3 + nk % 3), a template parameter so that each
@@ -127,11 +172,12 @@ using IC = std::integral_constant<int, V>;
 //   G (persistent only, gp set): tiles of key columns (n0 < hc*dim)
 //     end in the gate's partial sums instead of a store; value columns go to
 //     C at column n - hc*dim.
+// A rows: copied rows for BT >= 128, table rows at loaded offsets for BT = 64
+// (ASource).
 template <int BT, int WMV, int WNV, int L, bool P, bool G = false>
-__device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
+__device__ __forceinline__ void gathered_tile(const ASource as,
                                               const float2* __restrict__ scl, int n_cols,
-                                              int64_t m_pad, const uint8_t* __restrict__ table,
-                                              int64_t num_rows, const uint16_t* __restrict__ W,
+                                              int64_t m_pad, const uint16_t* __restrict__ W,
                                               int64_t M, int N, uint16_t* __restrict__ C,
                                               int64_t ldc, int tiles_m, int tiles_n, int per_xcd,
                                               const GatePartials& gp, uint8_t* smem) {
@@ -146,7 +192,8 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
     constexpr int OFF_W = OFF_SC + NW * G_NS * 256;
     constexpr int OFF_WQK = OFF_W + (BT / 8) * G_NS * 1024;  // q*k, 512 bytes per wave (G only)
     constexpr int NLOAD = NA + 1 + NB;  // DMA per wave per k-tile
-    constexpr int NIDS = NA;            // row-offset loads per wave per k-tile
+    constexpr bool CA = BT >= 128;      // copied rows (else table rows at offsets)
+    constexpr int NIDS = CA ? 0 : NA;   // row-offset loads per wave per k-tile
 
     const int K = n_cols * 64;
     const int nk = n_cols;
@@ -217,27 +264,31 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WNV, wn = wave % WNV;
 
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(aoff, (uint32_t)(n_cols * m_pad * 4));
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(as.src, as.src_bytes);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(as.aoff, CA ? 0u : (uint32_t)(n_cols * m_pad * 4));
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(scl, (uint32_t)(n_cols * m_pad * 8));
-    const __amdgpu_buffer_rsrc_t rt = make_rsrc(table, (uint32_t)(num_rows * 64));
     // W rows n0 .. n0+BT-1 (rows past N read as zeros)
     auto w_rsrc = [&](int n0x) {
         return make_rsrc(W + (int64_t)n0x * K, (uint32_t)(min(BT, N - n0x) * K * 2));
     };
-    const int col_o = (int)(m_pad * 4);  // aoff bytes per hash column
-    const int col_s = (int)(m_pad * 8);  // scl bytes per hash column
+    const int col_a = (int)(m_pad * 64);  // arows bytes per hash column
+    const int col_o = (int)(m_pad * 4);   // aoff bytes per hash column
+    const int col_s = (int)(m_pad * 8);   // scl bytes per hash column
 
     // DMA lanes.  fp8 A instruction i fills block NW*i + wave: rows
     // 16*(NW*i + wave) + lane/4, lane%4 picking the 16-byte slot (which holds
     // logical chunk slot64(row, lane%4)).  The scale instruction moves the 32
     // rows x 2 fp32 of rows 32*wave .. 32*wave+31.  W instruction i fills
     // block NW*i + wave: rows 8*(NW*i + wave) + lane/8.
-    uint32_t ao_v[NA], ach[NA];
+    // av: copied rows, the lane's byte within the k-tile's rows (+ (kt * m_pad
+    // + m0) * 64 in the scalar offset); table rows, the lane's aoff entry
+    // (+ kt * m_pad * 4 + m0 * 4 likewise) and ach its 16-byte chunk
+    uint32_t av[NA], ach[NA];
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
         const int row = 16 * (NW * i + wave) + (lane >> 2);
-        ao_v[i] = (uint32_t)(row * 4);  // + m0*4 in the scalar offset
         ach[i] = (uint32_t)slot64(row, lane & 3) * 16u;
+        av[i] = CA ? (uint32_t)(row * 64) + ach[i] : (uint32_t)(row * 4);
     }
     const uint32_t sc_v = (uint32_t)(32 * wave * 8 + lane * 4);  // + m0*8 likewise
     uint32_t wvoff[NB];
@@ -247,23 +298,29 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
         wvoff[i] = (uint32_t)(row * K * 2 + slot128(row, lane & 7) * 16);
     }
 
-    uint32_t id_a[NA];  // table byte offsets of the next k-tile to fetch
+    uint32_t id_a[NA];  // table rows: byte offsets of the next k-tile to fetch
     auto load_offs = [&](int kt, int m0x) {
+        if constexpr (!CA)
 #pragma unroll
-        for (int i = 0; i < NA; ++i)
-            id_a[i] = __builtin_amdgcn_raw_buffer_load_b32(ro, ao_v[i], kt * col_o + m0x * 4, 0);
+            for (int i = 0; i < NA; ++i)
+                id_a[i] = __builtin_amdgcn_raw_buffer_load_b32(ro, av[i], kt * col_o + m0x * 4, 0);
     };
     // part 0: the fp8 rows and the scales; parts 1 and 2: the two halves of
-    // the W rows (spread over the k-tile's first three k-steps)
+    // the W rows (spread over the k-tile's first three k-steps).  ia: the
+    // rows' table offsets (table rows only)
     auto issue_dma = [&](int kt, auto sd, const uint32_t* ia, int m0x, int n0x, auto partc) {
         constexpr int SD = decltype(sd)::value;
         constexpr int PART = decltype(partc)::value;
         if constexpr (PART == 0) {
 #pragma unroll
-            for (int i = 0; i < NA; ++i)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rt, (lds_void*)(smem + ((NW * i + wave) * G_NS + SD) * 1024), 16,
-                    ia[i] + ach[i], 0, 0, 0);
+            for (int i = 0; i < NA; ++i) {
+                lds_void* dst = (lds_void*)(smem + ((NW * i + wave) * G_NS + SD) * 1024);
+                if constexpr (CA)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, av[i],
+                                                             kt * col_a + m0x * 64, 0, 0);
+                else
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, ia[i] + ach[i], 0, 0, 0);
+            }
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rs, (lds_void*)(smem + OFF_SC + (wave * G_NS + SD) * 256), 4, sc_v,
                 kt * col_s + m0x * 8, 0, 0);
@@ -353,10 +410,11 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
     // from the fp8 read (k-steps 0 and 2 read nothing new for A, 1 and 3 read
     // the next pair's after converting), reads the next k-step's W fragments
     // and issues TI*TJ MFMAs (a fenced scheduling region).  At k-step 0 the
-    // row offsets of k-tile kt+3 are loaded and the DMA of k-tile kt+2's fp8
-    // rows and scales (whose offsets arrived one k-tile ago) is issued,
-    // offsets first so that waiting for them never waits for the newer DMA;
-    // k-steps 1 and 2 issue one half of its W rows each (every load of the
+    // DMA of k-tile kt+2's fp8 rows and scales is issued (copied rows: at
+    // computed addresses; table rows: at the offsets that arrived one k-tile
+    // ago, after loading k-tile kt+3's, so that waiting for the offsets
+    // never waits for the newer DMA), and k-steps 1 and 2 issue one half of
+    // its W rows each (every load of the
     // k-tile is still issued before its hand-over, and the two waves of a
     // SIMD do not both burst all their loads into one k-step).  The hand-over
     // barrier comes before the last k-step's MFMAs, once its fragments have
@@ -366,9 +424,10 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
     // MFMAs instead of between them was slower).
     //   WAITN: loads issued after k-tile kt+1's DMA that may stay in flight;
     //          -1 for the last k-tile (no hand-over).
+    //   LOAD_IDS (table rows): load the row offsets of k-tile kt+3.
     auto k_tile = [&](int kt, auto st, auto ldids, auto dma, auto waitn) {
         constexpr int S = decltype(st)::value;
-        constexpr bool LOAD_IDS = decltype(ldids)::value;
+        constexpr bool LOAD_IDS = decltype(ldids)::value && !CA;
         constexpr bool DMA = decltype(dma)::value;
         constexpr int WAITN = decltype(waitn)::value;
         auto step = [&](auto ksc) {
@@ -377,8 +436,9 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
             convert(cur);
             if constexpr (ks == 0 && DMA) {
                 uint32_t ia[NA];
+                if constexpr (!CA)
 #pragma unroll
-                for (int i = 0; i < NA; ++i) ia[i] = id_a[i];
+                    for (int i = 0; i < NA; ++i) ia[i] = id_a[i];
                 // persistent: past this tile's last k-tile, load the next tile's
                 const bool nx3 = P && kt + 3 >= nk, nx2 = P && kt + 2 >= nk;
                 if constexpr (LOAD_IDS) load_offs(nx3 ? kt + 3 - nk : kt + 3, nx3 ? m0n : m0c);
@@ -400,7 +460,8 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
             for (int r = 0; r < TI * TJ; ++r) {
                 if (r < TI) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (ks == 0 && DMA && r < 2) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+                if (ks == 0 && DMA && r < 2)
+                    __builtin_amdgcn_sched_group_barrier(0x020, CA ? 1 : 2, 0);
                 if (ks == 0 && DMA && r == 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
                 if ((ks == 1 || ks == 2) && DMA && r < NB / 2)
                     __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
@@ -432,14 +493,18 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
     };
     using T = std::true_type;
     using F = std::false_type;
+    // loads issued after k-tile kt+1's DMA when k-tile kt hands over: k-tile
+    // kt+3's offsets and kt+2's whole DMA (steady), kt+2's DMA alone (no
+    // offsets left to load), none (the last DMA'd k-tile), no hand-over after
+    // the last k-tile
     using Wsteady = IC<NIDS + NLOAD>;
     using W7 = IC<NLOAD>;
     using W0 = IC<0>;
     using Wn = IC<-1>;
 
-    // prologue: k-tiles 0 and 1 in flight, offsets of k-tile 2 loaded.  The
-    // W rows of both go first: they need no row offsets, so they stream
-    // while the offsets make their round trip.
+    // prologue: k-tiles 0 and 1 in flight (and for table rows the offsets of
+    // k-tile 2 loaded).  The W rows of both go first: they need no row
+    // offsets, so they stream while any offsets make their round trip.
     {
         issue_dma(0, IC<0>{}, nullptr, m0c, n0c, IC<1>{});
         issue_dma(0, IC<0>{}, nullptr, m0c, n0c, IC<2>{});
@@ -447,15 +512,17 @@ __device__ __forceinline__ void gathered_tile(const uint32_t* __restrict__ aoff,
             issue_dma(1, IC<1>{}, nullptr, m0c, n0c, IC<1>{});
             issue_dma(1, IC<1>{}, nullptr, m0c, n0c, IC<2>{});
         }
-        load_offs(0, m0c);
         uint32_t ia[NA];
+        load_offs(0, m0c);
+        if constexpr (!CA)
 #pragma unroll
-        for (int i = 0; i < NA; ++i) ia[i] = id_a[i];
+            for (int i = 0; i < NA; ++i) ia[i] = id_a[i];
         if (nk > 1) load_offs(1, m0c);
         issue_dma(0, IC<0>{}, ia, m0c, n0c, IC<0>{});
         if (nk > 1) {
+            if constexpr (!CA)
 #pragma unroll
-            for (int i = 0; i < NA; ++i) ia[i] = id_a[i];
+                for (int i = 0; i < NA; ++i) ia[i] = id_a[i];
             if (nk > 2) load_offs(2, m0c);
             issue_dma(1, IC<1>{}, ia, m0c, n0c, IC<0>{});
         }
@@ -712,25 +779,23 @@ static_assert(8 * 128 * 128 <= SMEM256 && 4 * 64 * 128 <= SMEM128, "epilogue sta
 
 template <int L, bool P, bool G>
 __global__ void __launch_bounds__(512, 1)
-wkv_gathered_256(const uint32_t* __restrict__ aoff, const float2* __restrict__ scl, int n_cols,
-                 int64_t m_pad, const uint8_t* __restrict__ table, int64_t num_rows,
+wkv_gathered_256(const ASource as, const float2* __restrict__ scl, int n_cols, int64_t m_pad,
                  const uint16_t* __restrict__ W, int64_t M, int N, uint16_t* __restrict__ C,
                  int64_t ldc, int tiles_m, int tiles_n, int per_xcd, GatePartials gp) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM256];
-    gathered_tile<256, 4, 2, L, P, G>(aoff, scl, n_cols, m_pad, table, num_rows, W, M, N, C, ldc,
+    gathered_tile<256, 4, 2, L, P, G>(as, scl, n_cols, m_pad, W, M, N, C, ldc,
                                       tiles_m, tiles_n, per_xcd, gp, smem);
 }
 
 template <int L>
 __global__ void __launch_bounds__(256, 1)
-wkv_gathered_128(const uint32_t* __restrict__ aoff, const float2* __restrict__ scl, int n_cols,
-                 int64_t m_pad, const uint8_t* __restrict__ table, int64_t num_rows,
+wkv_gathered_128(const ASource as, const float2* __restrict__ scl, int n_cols, int64_t m_pad,
                  const uint16_t* __restrict__ W, int64_t M, int N, uint16_t* __restrict__ C,
                  int64_t ldc, int tiles_m, int tiles_n, int per_xcd, const int* m_live) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM128];
     GatePartials lim{};
     lim.m_live = m_live;
-    gathered_tile<128, 2, 2, L, false>(aoff, scl, n_cols, m_pad, table, num_rows, W, M, N, C, ldc,
+    gathered_tile<128, 2, 2, L, false>(as, scl, n_cols, m_pad, W, M, N, C, ldc,
                                        tiles_m, tiles_n, per_xcd, lim, smem);
 }
 
@@ -740,20 +805,18 @@ constexpr int SMEM64 = (64 / 16) * G_NS * 1024 + 2 * G_NS * 256 + (64 / 8) * G_N
 
 template <int L>
 __global__ void __launch_bounds__(128)
-wkv_gathered_64(const uint32_t* __restrict__ aoff, const float2* __restrict__ scl, int n_cols,
-                int64_t m_pad, const uint8_t* __restrict__ table, int64_t num_rows,
+wkv_gathered_64(const ASource as, const float2* __restrict__ scl, int n_cols, int64_t m_pad,
                 const uint16_t* __restrict__ W, int64_t M, int N, uint16_t* __restrict__ C,
                 int64_t ldc, int tiles_m, int tiles_n, int per_xcd) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM64];
     const GatePartials none{};
-    gathered_tile<64, 2, 1, L, false>(aoff, scl, n_cols, m_pad, table, num_rows, W, M, N, C, ldc,
+    gathered_tile<64, 2, 1, L, false>(as, scl, n_cols, m_pad, W, M, N, C, ldc,
                                       tiles_m, tiles_n, per_xcd, none, smem);
 }
 
 template <int L>
-hipError_t run_gathered_l(int bt, const uint32_t* aoff, const float2* scl, int n_cols,
-                          int64_t m_pad, const uint8_t* table, int64_t num_rows,
-                          const uint16_t* w, int64_t M, int N, uint16_t* c, int64_t ldc,
+hipError_t run_gathered_l(int bt, const ASource& as, const float2* scl, int n_cols,
+                          int64_t m_pad, const uint16_t* w, int64_t M, int N, uint16_t* c, int64_t ldc,
                           hipStream_t s, const int* m_live) {
     const int tiles_m = (int)((M + bt - 1) / bt);
     const int tiles_n = (N + bt - 1) / bt;
@@ -761,27 +824,27 @@ hipError_t run_gathered_l(int bt, const uint32_t* aoff, const float2* scl, int n
     const int per_xcd = (total + N_XCD - 1) / N_XCD;
     if (bt == 256)
         wkv_gathered_256<L, false, false><<<dim3(per_xcd * N_XCD), dim3(512), 0, s>>>(
-            aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, tiles_m, tiles_n, per_xcd,
+            as, scl, n_cols, m_pad, w, M, N, c, ldc, tiles_m, tiles_n, per_xcd,
             GatePartials{});
     else if (bt == 64)
         wkv_gathered_64<L><<<dim3(per_xcd * N_XCD), dim3(128), 0, s>>>(
-            aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, tiles_m, tiles_n, per_xcd);
+            as, scl, n_cols, m_pad, w, M, N, c, ldc, tiles_m, tiles_n, per_xcd);
     else
         wkv_gathered_128<L><<<dim3(per_xcd * N_XCD), dim3(256), 0, s>>>(
-            aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, tiles_m, tiles_n, per_xcd,
+            as, scl, n_cols, m_pad, w, M, N, c, ldc, tiles_m, tiles_n, per_xcd,
             m_live);
     return hipGetLastError();
 }
 
-hipError_t run_gathered(int bt, const uint32_t* aoff, const float2* scl, int n_cols,
-                        int64_t m_pad, const uint8_t* table, int64_t num_rows, const uint16_t* w,
+hipError_t run_gathered(int bt, const ASource& as, const float2* scl, int n_cols,
+                        int64_t m_pad, const uint16_t* w,
                         int64_t M, int N, uint16_t* c, int64_t ldc, hipStream_t s,
                         const int* m_live = nullptr) {
     // m_live (compacted rows) is honoured by the 128-wide tiles only
     if (m_live && bt != 128) return hipErrorInvalidValue;
     const int L = n_cols <= 2 ? n_cols : 3 + n_cols % 3;
 #define ENGRAM_RUN_L(V) \
-    run_gathered_l<V>(bt, aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, s, m_live)
+    run_gathered_l<V>(bt, as, scl, n_cols, m_pad, w, M, N, c, ldc, s, m_live)
     switch (L) {
         case 1: return ENGRAM_RUN_L(1);
         case 2: return ENGRAM_RUN_L(2);
@@ -795,8 +858,8 @@ hipError_t run_gathered(int bt, const uint32_t* aoff, const float2* scl, int n_c
 // Persistent 256x256 launch: one workgroup per compute unit (a multiple of 8,
 // so every XCD gets the same number), each running its XCD's tiles
 // slot, slot + nwg, ...  Needs nk % 3 == 0 and N a multiple of 256.
-hipError_t run_persistent(const uint32_t* aoff, const float2* scl, int n_cols, int64_t m_pad,
-                          const uint8_t* table, int64_t num_rows, const uint16_t* w, int64_t M,
+hipError_t run_persistent(const ASource& as, const float2* scl, int n_cols, int64_t m_pad,
+                          const uint16_t* w, int64_t M,
                           int N, uint16_t* c, int64_t ldc, int cus, const GatePartials& gp,
                           hipStream_t s) {
     const int tiles_m = (int)((M + 255) / 256);
@@ -807,23 +870,25 @@ hipError_t run_persistent(const uint32_t* aoff, const float2* scl, int n_cols, i
     if (grid > per_xcd * N_XCD) grid = per_xcd * N_XCD;
     if (gp.x)
         wkv_gathered_256<3, true, true><<<dim3(grid), dim3(512), 0, s>>>(
-            aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, tiles_m, tiles_n, per_xcd,
+            as, scl, n_cols, m_pad, w, M, N, c, ldc, tiles_m, tiles_n, per_xcd,
             gp);
     else
         wkv_gathered_256<3, true, false><<<dim3(grid), dim3(512), 0, s>>>(
-            aoff, scl, n_cols, m_pad, table, num_rows, w, M, N, c, ldc, tiles_m, tiles_n, per_xcd,
+            as, scl, n_cols, m_pad, w, M, N, c, ldc, tiles_m, tiles_n, per_xcd,
             gp);
     return hipGetLastError();
 }
 
-hipError_t launch_prep(const Geom& g, const int32_t* hash_ids, const uint8_t* scales, int64_t M,
-                       int64_t m_pad, uint32_t* aoff, float2* scl, uint32_t* err, hipStream_t s,
+hipError_t launch_prep(const Geom& g, const int32_t* hash_ids, const uint8_t* table,
+                       const uint8_t* scales, int64_t M, int64_t m_pad, uint8_t* arows,
+                       uint32_t* aoff, float2* scl, uint32_t* err, hipStream_t s,
                        const uint16_t* q = nullptr, const uint16_t* k = nullptr,
                        float* wqk = nullptr, const int32_t* live_idx = nullptr,
                        const int* m_live = nullptr) {
     const int64_t total = (int64_t)g.n_cols * m_pad;
     prep_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s>>>(
-        hash_ids, g.n_cols, M, m_pad, scales, g.num_embeddings, aoff, scl, err, q, k, wqk,
+        hash_ids, g.n_cols, M, m_pad, table, scales, g.num_embeddings, arows, aoff, scl, err, q,
+        k, wqk,
         g.hc * g.dim, live_idx, m_live);
     return hipGetLastError();
 }
@@ -855,17 +920,23 @@ bool persistent_ok(const Geom& g, int64_t M, int nbig, int cus) {
 
 }  // namespace
 
-// 32-bit buffer offsets: the table must stay below 4 GiB and each scratch
-// array below 2 GiB (its per-column offsets are 32-bit signed scalars)
+// 32-bit buffer offsets: copied rows stay below 2 GiB (their offsets within
+// the array are 32-bit signed scalars; the copies read the table with 64-bit
+// addresses); with row offsets the table stays below 4 GiB and each array
+// below 2 GiB
 bool gathered_supported(const Geom& g, int64_t M) {
-    return g.head_dim == 64 && g.num_embeddings * 64 < ((int64_t)1 << 32) &&
-           (int64_t)g.n_cols * padded_rows(M) * 8 < ((int64_t)1 << 31);
+    if (g.head_dim != 64) return false;
+    const int64_t rows = (int64_t)g.n_cols * padded_rows(M);
+    if (M > kOffsetRowsMax) return rows * 64 < ((int64_t)1 << 31);
+    return g.num_embeddings * 64 < ((int64_t)1 << 32) && rows * 8 < ((int64_t)1 << 31);
 }
 
-// aoff (uint32) then scl (2 x fp32) per (hash column, padded row), then
-// q*k in fp32 per (stream, feature) for the gate partials
+// per (hash column, padded row): the copied row (64 bytes) or its offset
+// (4), then its scales (8); then q*k in fp32 per (stream, feature) for the
+// gate partials
 size_t gathered_scratch_bytes(const Geom& g, int64_t M) {
-    return (size_t)g.n_cols * (size_t)padded_rows(M) * 12 + (size_t)g.hc * g.dim * 4;
+    const size_t per = M > kOffsetRowsMax ? 72 : 12;
+    return (size_t)g.n_cols * (size_t)padded_rows(M) * per + (size_t)g.hc * g.dim * 4;
 }
 
 // Same tiling policy as the bf16 projection: 256 x 256 tiles over the widest
@@ -875,19 +946,36 @@ size_t gathered_scratch_bytes(const Geom& g, int64_t M) {
 GatheredScratch gathered_scratch(const Geom& g, int64_t M, void* base) {
     GatheredScratch r;
     r.m_pad = padded_rows(M);
-    r.aoff = reinterpret_cast<uint32_t*>(base);
-    r.scl = reinterpret_cast<float2*>(r.aoff + (int64_t)g.n_cols * r.m_pad);
+    const int64_t rows = (int64_t)g.n_cols * r.m_pad;
+    if (M > kOffsetRowsMax) {
+        r.arows = reinterpret_cast<uint8_t*>(base);
+        r.aoff = nullptr;
+        r.scl = reinterpret_cast<float2*>(r.arows + rows * 64);
+    } else {
+        r.arows = nullptr;
+        r.aoff = reinterpret_cast<uint32_t*>(base);
+        r.scl = reinterpret_cast<float2*>(r.aoff + rows);
+    }
     r.wqk = reinterpret_cast<float*>(r.scl + (int64_t)g.n_cols * r.m_pad);
     return r;
 }
 
-hipError_t launch_prep_scratch(const Geom& g, const int32_t* hash_ids, const uint8_t* scales,
-                               int64_t M, void* scratch, uint32_t* err, hipStream_t s,
+// The projection's A source for scratch gs: the copied rows, or the table
+// at the row offsets.
+ASource a_source(const Geom& g, const GatheredScratch& gs, const uint8_t* table) {
+    if (gs.arows) return ASource{gs.arows, nullptr, (uint32_t)(g.n_cols * gs.m_pad * 64)};
+    return ASource{table, gs.aoff, (uint32_t)(g.num_embeddings * 64)};
+}
+
+hipError_t launch_prep_scratch(const Geom& g, const int32_t* hash_ids, const uint8_t* table,
+                               const uint8_t* scales, int64_t M, void* scratch, uint32_t* err,
+                               hipStream_t s,
                                const uint16_t* q, const uint16_t* k, const int32_t* live_idx,
                                const int* m_live) {
     if (M == 0) return hipSuccess;
     const GatheredScratch gs = gathered_scratch(g, M, scratch);
-    return launch_prep(g, hash_ids, scales, M, gs.m_pad, gs.aoff, gs.scl, err, s, q, k,
+    return launch_prep(g, hash_ids, table, scales, M, gs.m_pad, gs.arows, gs.aoff, gs.scl, err,
+                       s, q, k,
                        q ? gs.wqk : nullptr, live_idx, m_live);
 }
 
@@ -897,28 +985,26 @@ hipError_t launch_wkv_gathered(const Geom& g, const int32_t* hash_ids, const uin
     if (M == 0) return hipSuccess;
     const GatheredScratch gs = gathered_scratch(g, M, scratch);
     const int64_t m_pad = gs.m_pad;
-    uint32_t* aoff = gs.aoff;
     float2* scl = gs.scl;
     if (!prepared) {
-        hipError_t e = launch_prep(g, hash_ids, scales, M, m_pad, aoff, scl, err, s);
+        hipError_t e = launch_prep(g, hash_ids, table, scales, M, m_pad, gs.arows, gs.aoff, scl,
+                                   err, s);
         if (e != hipSuccess) return e;
     }
-    if (M <= 256)  // decode-sized: the weight stream dominates; small tiles, many workgroups
-        return run_gathered(64, aoff, scl, g.n_cols, m_pad, table, g.num_embeddings, w, M, g.N,
-                            kv, g.N, s);
+    const ASource as = a_source(g, gs, table);
+    if (M <= kOffsetRowsMax)  // decode-sized: the weight stream dominates; small tiles
+        return run_gathered(64, as, scl, g.n_cols, m_pad, w, M, g.N, kv, g.N, s);
     const int N = g.N;
     const int cus = cu_count();
     const int nbig = big_columns(M, N, cus);
     hipError_t e;
     if (persistent_ok(g, M, nbig, cus))
-        e = run_persistent(aoff, scl, g.n_cols, m_pad, table, g.num_embeddings, w, M, nbig, kv, N,
-                           cus, GatePartials{}, s);
+        e = run_persistent(as, scl, g.n_cols, m_pad, w, M, nbig, kv, N, cus, GatePartials{}, s);
     else
-        e = run_gathered(256, aoff, scl, g.n_cols, m_pad, table, g.num_embeddings, w, M, nbig, kv,
-                         N, s);
+        e = run_gathered(256, as, scl, g.n_cols, m_pad, w, M, nbig, kv, N, s);
     if (e != hipSuccess || nbig >= N) return e;
-    return run_gathered(128, aoff, scl, g.n_cols, m_pad, table, g.num_embeddings,
-                        w + (int64_t)nbig * g.K, M, N - nbig, kv + nbig, N, s);
+    return run_gathered(128, as, scl, g.n_cols, m_pad, w + (int64_t)nbig * g.K, M, N - nbig,
+                        kv + nbig, N, s);
 }
 
 bool gate_partials_supported(const Geom& g, int64_t M) {
@@ -942,24 +1028,22 @@ hipError_t launch_wkv_gate_partials(const Geom& g, const int32_t* hash_ids, cons
         return hipErrorInvalidValue;
     const GatheredScratch gs = gathered_scratch(g, M, scratch);
     const int64_t m_pad = gs.m_pad;
-    uint32_t* aoff = gs.aoff;
     float2* scl = gs.scl;
     float* wqk = gs.wqk;
     hipError_t e = prepared ? hipSuccess
-                            : launch_prep(g, hash_ids, scales, M, m_pad, aoff, scl, err, s, gp.q,
-                                          gp.k, wqk);
+                            : launch_prep(g, hash_ids, table, scales, M, m_pad, gs.arows, gs.aoff,
+                                          scl, err, s, gp.q, gp.k, wqk);
     if (e != hipSuccess) return e;
     const int cus = cu_count();
     const int nbig = big_columns(M, g.N, cus);
     const int kcols = g.hc * g.dim;
     GatePartials gpw = gp;
     gpw.wqk = wqk;
-    e = run_persistent(aoff, scl, g.n_cols, m_pad, table, g.num_embeddings, w, M, nbig, v, g.dim,
-                       cus, gpw, s);
+    const ASource as = a_source(g, gs, table);
+    e = run_persistent(as, scl, g.n_cols, m_pad, w, M, nbig, v, g.dim, cus, gpw, s);
     if (e != hipSuccess || nbig >= g.N) return e;
-    return run_gathered(128, aoff, scl, g.n_cols, m_pad, table, g.num_embeddings,
-                        w + (int64_t)nbig * g.K, M, g.N - nbig, v + (nbig - kcols), g.dim, s,
-                        gp.m_live);
+    return run_gathered(128, as, scl, g.n_cols, m_pad, w + (int64_t)nbig * g.K, M, g.N - nbig,
+                        v + (nbig - kcols), g.dim, s, gp.m_live);
 }
 
 }  // namespace engram

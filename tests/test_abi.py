@@ -155,8 +155,11 @@ def test_fused_projection_host_checks():
     g = good()
     fake = C.c_void_p(1 << 20)
     need = ge.engram_wkv_gathered_scratch_size(g, 4096)
-    assert need == 24 * 4096 * 12 + 4 * 5120 * 4
+    assert need == 24 * 4096 * 72 + 4 * 5120 * 4
+    # decode-sized batches keep row offsets (12 bytes a row), larger ones copy rows (72)
     assert ge.engram_wkv_gathered_scratch_size(g, 1) == 24 * 256 * 12 + 4 * 5120 * 4
+    assert ge.engram_wkv_gathered_scratch_size(g, 256) == 24 * 256 * 12 + 4 * 5120 * 4
+    assert ge.engram_wkv_gathered_scratch_size(g, 257) == 24 * 512 * 72 + 4 * 5120 * 4
 
     def call(g=g, M=16, scratch=fake, nbytes=1 << 30, table=fake):
         return lib.engram_wkv_gathered(C.byref(g), table, fake, fake, M, fake, fake, scratch,
@@ -172,8 +175,10 @@ def test_fused_projection_host_checks():
     h.head_dim = 32                                        # one row is not one k-tile
     assert call(g=h) == 2
     h = good()
-    h.num_embeddings = (1 << 26) + 1                       # table beyond 32-bit offsets
+    h.num_embeddings = (1 << 26) + 1                       # decode-sized: table offsets 32-bit
     assert call(g=h) == 2
+    # larger batches: the copied rows' offsets are 32-bit (24 columns x 64 bytes x rows)
+    assert call(M=(1 << 31) // (24 * 64)) == 2
     # small batches: the forward's workspace also holds the fused scratch
     assert ge.engram_forward_workspace_size(g, 1) >= 256 + 24 * 256 * 12
 
