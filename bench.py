@@ -280,6 +280,31 @@ def time_launches(fn, n, stream):
     return start.elapsed_time(end) / n * 1e-3  # seconds per launch
 
 
+def time_gpu(fn, n, stream):
+    """Seconds per call of fn on the GPU alone, for the stage and kernel
+    figures (the headline steps keep time_launches): the n calls are captured
+    once in a HIP graph and the graph is replayed, so they run back to back
+    with no host launch gaps between them (a call shorter than its host-side
+    launch cost would otherwise be timed at the host's pace).  fn must be
+    capture-safe: the library calls allocate nothing and never synchronise."""
+    import torch
+    graph = torch.cuda.CUDAGraph()
+    fn()  # anything lazily set up happens outside the capture
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        for _ in range(n):
+            fn()
+    graph.replay()  # warm
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    graph.replay()
+    end.record(stream)
+    end.synchronize()
+    del graph
+    return start.elapsed_time(end) / n * 1e-3
+
+
 # ------------------------------------------------------------------ profile summaries
 COPY_BYTES = 1 << 30
 FUSED_KERNELS = ("prep_kernel", "wkv_gathered_256<3, true, true>", "wkv_gathered_128")
@@ -556,18 +581,18 @@ def main():
     ge.engram_gate_add(g, x, kv, q, k, mask=mask, out=out)
     torch.cuda.synchronize()
     reps = max(args.steps, 50)
-    st_gather = time_launches(lambda: ge.engram_gather(g, table, scales, hid, rows=rows), reps, stream)
-    st_wkv = time_launches(lambda: ge.engram_wkv(g, rows, w, kv=kv), reps, stream)
-    st_fused = time_launches(
+    st_gather = time_gpu(lambda: ge.engram_gather(g, table, scales, hid, rows=rows), reps, stream)
+    st_wkv = time_gpu(lambda: ge.engram_wkv(g, rows, w, kv=kv), reps, stream)
+    st_fused = time_gpu(
         lambda: ge.engram_wkv_gathered(g, table, scales, hid, w, kv=kv, scratch=scratch), reps,
         stream)
-    st_gate = time_launches(lambda: ge.engram_gate_add(g, x, kv, q, k, mask=mask, out=out), reps,
+    st_gate = time_gpu(lambda: ge.engram_gate_add(g, x, kv, q, k, mask=mask, out=out), reps,
                             stream)
-    st_hash = time_launches(lambda: ge.engram_hash(g, tables, ids, hash_ids=hid), reps, stream)
-    st_proj = time_launches(
+    st_hash = time_gpu(lambda: ge.engram_hash(g, tables, ids, hash_ids=hid), reps, stream)
+    st_proj = time_gpu(
         lambda: ge.engram_wkv_gate_partials(g, table, scales, hid, w, xf, q, k, v=v, part=part,
                                             scratch=scratch), reps, stream)
-    st_pgate = time_launches(
+    st_pgate = time_gpu(
         lambda: ge.engram_gate_from_partials(g, xf, v, part, mask=mask, out=outf), reps, stream)
 
     for _ in range(args.warmup):
@@ -711,8 +736,8 @@ def decode(args):
     kv = torch.empty((B, g.N), dtype=torch.bfloat16, device=dev)
     scratch = torch.empty(ge.engram_wkv_gathered_scratch_size(g, B), dtype=torch.uint8, device=dev)
     ge.engram_wkv_gathered(g, table, scales, hid, w, kv=kv, scratch=scratch)
-    st_proj = time_launches(lambda: ge.engram_wkv_gathered(g, table, scales, hid, w, kv=kv,
-                                                           scratch=scratch), 200, stream)
+    st_proj = time_gpu(lambda: ge.engram_wkv_gathered(g, table, scales, hid, w, kv=kv,
+                                                      scratch=scratch), 200, stream)
     proj_bytes = g.N * g.K * 2 + B * g.n_hash_cols * (64 + 2) + B * g.N * 2
     if args.copy_calibration:  # a 1 GiB copy for the counter runs to scale by
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -805,21 +830,21 @@ def long_mixed(args):
         ge.engram_gate_from_partials(g, xf, v, part, mask=mask.reshape(-1), out=outf)
 
     dense()
-    sec_dense = time_launches(dense, steps, stream)
+    sec_dense = time_gpu(dense, steps, stream)
     # the projection over the live positions alone
     live = torch.from_numpy(np.nonzero(mask_np.reshape(-1))[0]).to(dev)
     n_live = int(live.numel())
     hid_l = hid.index_select(0, live).contiguous()
     x_l = xf.index_select(0, live).contiguous()
     v_l, part_l = ge.engram_wkv_gate_partials(g, table, scales, hid_l, w, x_l, q, k)
-    sec_proj = time_launches(
+    sec_proj = time_gpu(
         lambda: ge.engram_wkv_gate_partials(g, table, scales, hid_l, w, x_l, q, k, v=v_l,
                                             part=part_l), steps, stream)
     achieved = 2 * g.K * g.N * n_live / sec_proj / 1e12
     # the row gather on its own over every position (Zipf ids: rows repeat)
     rows = ge.engram_gather(g, table, scales, hid)
-    sec_gather = time_launches(lambda: ge.engram_gather(g, table, scales, hid, rows=rows), steps,
-                               stream)
+    sec_gather = time_gpu(lambda: ge.engram_gather(g, table, scales, hid, rows=rows), steps,
+                          stream)
     gather_read = n_tok * g.n_hash_cols * (g.head_dim + g.head_dim // 32)
     gather_write = n_tok * g.K * 2
     # the forward with out aliasing x (a masked position is then not touched);
