@@ -148,13 +148,15 @@ engram_status engram_wkv(const engram_geometry* g, const uint16_t* a, const uint
  * exactly what engram_gather writes (each dequantised element is the same
  * bf16 value) and the sum is the one engram_wkv takes.  The bf16 rows never
  * reach memory.  Requires head_dim == 64 (one table row per 64-wide k-tile)
- * and n_hash_cols * roundup(M, 256) * 64 < 2^31; otherwise
+ * and, with P = n_hash_cols * roundup(M, 256): for M > 256, P * 64 < 2^31;
+ * for M <= 256, P * 8 < 2^31 and num_embeddings * 64 < 2^32; otherwise
  * ENGRAM_ERR_UNSUPPORTED (use engram_gather + engram_wkv).
  *   table, scales, hash_ids as in engram_gather; w, kv as in engram_wkv.
  *   scratch  device memory of engram_wkv_gathered_scratch_size(g, M) bytes,
- *            256-byte aligned (each gathered row's 64 fp8 codes and its two
- *            scales, regrouped per hash column: 72 bytes per position,
- *            rounded up to 256 positions, and column; then q*k in fp32);
+ *            256-byte aligned: per hash column and position (rounded up to
+ *            256 positions), for M > 256 the row's 64 fp8 codes copied from
+ *            the table, for M <= 256 its byte offset in the table (4 bytes),
+ *            then its two scales as fp32 (8 bytes); then q*k in fp32;
  *            contents on entry do not matter.
  * An id outside [0, num_embeddings) reads as a zero row and sets
  * ENGRAM_ERRBIT_ROW in *err (if err is not NULL). */
