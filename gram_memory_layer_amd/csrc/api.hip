@@ -116,7 +116,7 @@ engram_status forward_launch(const engram_geometry* g, const engram_hash_tables*
     // projection otherwise
     const bool fused = aligned16(table) && engram::gathered_supported(gg, n_tok);
     if (fused && engram::gate_partials_supported(gg, n_tok)) {
-        // fully fused: the hash writes the projection's row offsets and
+        // fully fused: the hash writes the projection's copied rows and
         // scales directly; the projection reduces the key columns into the
         // gate's partial sums and stores only the value; kv's region holds both
         // With a mask, only live positions are projected: they are packed
