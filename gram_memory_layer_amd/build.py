@@ -3,12 +3,14 @@
     python -m gram_memory_layer_amd.build
 
 Each csrc/*.hip file is compiled to an object in parallel, then linked into
-gram_memory_layer_amd/libengram.so.  Always rebuilds.
+gram_memory_layer_amd/libengram.so.  Always rebuilds, and refuses a kernel
+that uses scratch memory (by the compiler's resource-usage remarks).
 """
 from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -36,12 +38,31 @@ def hipcc() -> str:
     return p
 
 
+def _scratch_kernels(remarks: str) -> list:
+    """Kernels whose resource-usage remarks report scratch (private) memory:
+    a spill or a local array placed there costs every launch its scratch
+    set-up and every access a memory round trip."""
+    found, name = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name and int(m.group(1)) > 0:
+            found.append("%s (%s bytes a lane)" % (name, m.group(1)))
+    return found
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + FLAGS + ["-c", src, "-o", obj]
+    cmd = [hipcc()] + FLAGS + ["-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, r.stdout, r.stderr))
+    spills = _scratch_kernels(r.stderr)
+    if spills:
+        raise RuntimeError("%s: kernels using scratch memory:\n  %s" % (src, "\n  ".join(spills)))
     return obj
 
 

@@ -477,7 +477,7 @@ hipError_t launch_wkv(const uint16_t* a, const uint16_t* w, int64_t M, int N, in
     if (M == 0) return hipSuccess;
     if (M >= 1024 && K % BK == 0 && (int64_t)K * 2 * 256 < (1ll << 31))
         return run_main(a, w, M, N, K, kv, s);
-    if (M >= 1024) return run<256, 256, 128, 128>(a, w, M, N, K, kv, s);
+    if (M >= 1024) return run<256, 256, 128, 64>(a, w, M, N, K, kv, s);
     return run<64, 64, 32, 32>(a, w, M, N, K, kv, s);
 }
 

@@ -215,3 +215,19 @@ def test_forward_noalloc_host_checks():
     assert call(1, big) == 5
     g.head_dim = 40
     assert call(1, 8) == 2
+
+
+def test_build_refuses_kernels_that_use_scratch():
+    # the build reads the compiler's resource-usage remarks and refuses any
+    # kernel with scratch memory (a spill or a local array placed there)
+    from gram_memory_layer_amd import build
+    remarks = "\n".join([
+        "x.hip:1:1: remark: Function Name: _Z6kernelAv [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:9:1: remark: Function Name: _Z6kernelBv [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:9:1: remark:     VGPRs: 512 [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:9:1: remark:     ScratchSize [bytes/lane]: 12 [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    found = build._scratch_kernels(remarks)
+    assert len(found) == 1 and found[0].startswith("_Z6kernelBv")
+    assert build._scratch_kernels("") == []
