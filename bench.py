@@ -732,6 +732,28 @@ def decode(args):
     wall = time.perf_counter() - t0
     eager = time_launches(steps, 2, stream) / S
 
+    # the block's own forward takes hash ids (one engram_hash_layers launch
+    # serves every layer of a step): the same 128 steps from their hash ids
+    hstate = state0.clone()
+    hids = [ge.engram_hash(g, tables, ids[s], state=hstate) for s in range(S)]
+
+    def steps_hashed():
+        for s in range(S):
+            ge.engram_forward_hashed(g, table, scales, w, q, k, xs[s], hids[s], out=out,
+                                     workspace=ws)
+
+    with torch.cuda.stream(side):
+        steps_hashed()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph_h = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph_h):
+        steps_hashed()
+    for _ in range(2):
+        graph_h.replay()
+    sec_hashed = time_launches(graph_h.replay, reps, stream) / S
+    del graph_h
+
     hid = ge.engram_hash(g, tables, ids[0])
     kv = torch.empty((B, g.N), dtype=torch.bfloat16, device=dev)
     scratch = torch.empty(ge.engram_wkv_gathered_scratch_size(g, B), dtype=torch.uint8, device=dev)
@@ -761,6 +783,7 @@ def decode(args):
                      "unit": "GB/s", "frac": round(proj_bytes / st_proj / 1e9 / PEAK_HBM_GBS, 4),
                      "traffic": traffic_record(B, DECODE_TRAFFIC_FILE)},
         "eager_ms_per_step": round(eager * 1e3, 4),
+        "from_hash_ids_ms_per_step": round(sec_hashed * 1e3, 4),
         "projection_us": round(st_proj * 1e6, 2),
         "wall_s": round(wall, 3),
     }
