@@ -41,7 +41,7 @@ namespace engram {
 namespace {
 
 constexpr int G_NS = 3;                   // stages in the LDS ring
-constexpr int G_GROUP_M = 4;              // M-tiles per group in the tile order
+constexpr int G_GROUP_M = 8;              // M-tiles per group in the tile order
 
 // 16-byte slot of logical chunk c (0..3) in a 64-byte LDS row.  A fragment
 // read is one 16-byte chunk of 32 consecutive rows; the XOR term is a
