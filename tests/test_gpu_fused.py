@@ -124,15 +124,18 @@ def test_fused_every_scale_code(ge, dev):
     assert torch.equal(kv.view(torch.int16)[~nan_f], two.view(torch.int16)[~nan_t])
 
 
-def test_fused_bad_ids_read_zero_rows(ge, dev):
+# both row forms: decode-sized batches (table rows at offsets) and larger
+# ones (rows copied per hash column)
+@pytest.mark.parametrize("M", [100, 1100])
+def test_fused_bad_ids_read_zero_rows(ge, dev, M):
     cfg, rows = _small(256, 3, 3, 1, rows=3000)
     g = geometry(ge, cfg, rows)
-    say("fused bad ids")
+    say("fused bad ids M", M)
     table, scales = synth.embedding_table(cfg, rows, dev)
     w = synth.wkv_weight(cfg, dev)
     rng = np.random.default_rng(5)
-    h = rng.integers(0, rows, (1100, g.n_hash_cols)).astype(np.int32)
-    h[3, 0], h[700, 1], h[1099, 0] = -1, rows, 1 << 30
+    h = rng.integers(0, rows, (M, g.n_hash_cols)).astype(np.int32)
+    h[3, 0], h[M // 2, 1], h[M - 1, 0] = -1, rows, 1 << 30
     hid = torch.from_numpy(h).to(dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
     kv = ge.engram_wkv_gathered(g, table, scales, hid, w, err=err)
